@@ -1,0 +1,71 @@
+"""FP4Quant group codec (oracle; test infrastructure only).
+
+Follows "FP4Quant speeds up GPU communication, with a measurable accuracy
+trade-off": section "Why four bits need more than rounding" (split the
+tensor into small contiguous groups; a group scale from the root-mean-square
+magnitude; a normalized Walsh-Hadamard transform built from additions and
+subtractions; a second scale from the largest absolute transformed value
+that fits the group into the four-bit range; both scales travel with the
+codes; the transform is reversible, the rounding is not) and section
+"Making compression cheap enough to help" (receiver: unpack, dequantize,
+inverse transform).  Group sizes 64 and 256 are the ones the results section
+measures.
+
+Arithmetic is float64 throughout; the two scales are emitted as float32.
+The transform is a matrix product with scipy's Sylvester-ordered Hadamard
+matrix, a library routine.
+"""
+import numpy as np
+import scipy.linalg
+
+from . import formats as F
+
+
+def hadamard(G):
+    """Sylvester (natural) order: H[i, j] = (-1)**popcount(i & j)."""
+    return scipy.linalg.hadamard(G).astype(np.float64)
+
+
+def encode(x, G):
+    """x: float32 [R, C] (C % G == 0, G a power of two).
+
+    Per group g (G contiguous elements of a row):
+      s1 = sqrt(mean(x**2))      [reading] no epsilon; s1 == 0 -> zeros
+      y  = x / s1
+      z  = H y / sqrt(G)         [reading] orthonormal "normalized" WHT
+      s2 = max|z| / 6            [reading] absmax-to-6, E2M1's largest value
+      code = E2M1 RTN(z / s2)    [reading] no stochastic rounding here
+    Returns (codes uint8 [R, C], s1 float32 [R, C/G], s2 float32 [R, C/G])."""
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    R, C = x.shape
+    assert C % G == 0
+    xg = x.reshape(-1, G)
+    H = hadamard(G)
+    s1 = np.sqrt(np.mean(xg * xg, axis=1))
+    zero = s1 == 0
+    s1_safe = np.where(zero, 1.0, s1)
+    y = xg / s1_safe[:, None]
+    z = (y @ H.T) / np.sqrt(G)
+    s2 = np.max(np.abs(z), axis=1) / 6.0
+    s2_safe = np.where(zero | (s2 == 0), 1.0, s2)
+    codes = F.e2m1_rtn(z / s2_safe[:, None])
+    codes[zero] = 0
+    s1 = np.where(zero, 0.0, s1)
+    s2 = np.where(zero, 0.0, s2)
+    return (codes.reshape(R, C), s1.astype(np.float32).reshape(R, C // G),
+            s2.astype(np.float32).reshape(R, C // G))
+
+
+def decode64(codes, s1, s2, G):
+    """Receiver in float64: z' = e2m1 * s2; y' = H z' / sqrt(G); x' = y' * s1.
+    (H / sqrt(G) is its own inverse.)  Scales are the emitted float32 ones."""
+    codes = np.asarray(codes)
+    R, C = codes.shape
+    zq = F.e2m1_decode(codes).reshape(-1, G) * np.asarray(s2, np.float64).reshape(-1, 1)
+    y = (zq @ hadamard(G).T) / np.sqrt(G)
+    return (y * np.asarray(s1, np.float64).reshape(-1, 1)).reshape(R, C)
+
+
+def encode_packed(x, G):
+    codes, s1, s2 = encode(x, G)
+    return F.pack_codes(codes), s1, s2

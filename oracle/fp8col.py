@@ -1,0 +1,54 @@
+"""MXFP4 rows -> FP8 E4M3 columns, per ragged expert shard (oracle; test
+infrastructure only).
+
+Follows the report on "Practical FP4 Training for Large-Scale MoE Models on
+Hopper GPUs": "核心技术贡献" item 1 (direct FP4-to-FP8 conversion: 32-element
+MXFP4 blocks and 128-element FP8 blocks; the target scale of an FP8 block is
+the maximum of its four source block scales and each value's exponent is
+compensated by the difference, keeping the value), item 2 (FP4RowToFP8Col:
+dequantize, transpose and requantize in one pass) and item 3 (ragged expert
+shards addressed through precomputed offsets), and "通信量" (FP8 traffic about
+1.03 M K bytes, i.e. 4-byte scales per 128 elements).
+
+Definition used here (the value-level meaning of the bit remap):
+  for expert e with tokens [off[e], off[e+1]), token t, FP8 block b
+  (hidden channels 128b .. 128b+127 of that token = four MXFP4 blocks):
+    S_tgt = max of the four UE8M0 bytes;   d = S_tgt - S_sub >= 0
+    out[h, t - off[e]] = e4m3_RNE_sat( e2m1(code[t, h]) * 2**-d )   (float64)
+    fp32 scale[b, t - off[e]] = 2**(S_tgt - 127)
+[reading] "FP8 column": after the per-expert transpose to [H, n_e] a block is
+128 consecutive rows of one column.  The fp8 output of expert e starts at
+byte H*off[e]; its scales start at element (H/128)*off[e].
+"""
+import numpy as np
+
+from . import formats as F
+
+
+def convert(packed, scale_bytes, offsets, H):
+    """packed uint8 [T, H/2]; scale_bytes uint8 [T, H/32]; offsets int64 [E+1].
+    Returns (fp8 bytes uint8 [T*H], fp32 scales float32 [T*H/128])."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    sb = np.asarray(scale_bytes, dtype=np.uint8).astype(np.int64)
+    off = np.asarray(offsets, dtype=np.int64)
+    T = packed.shape[0]
+    assert H % 128 == 0 and packed.shape[1] * 2 == H and sb.shape == (T, H // 32)
+    if (sb == 0xFF).any():
+        raise ValueError("UE8M0 NaN scale is outside the contract")
+    out = np.zeros(T * H, dtype=np.uint8)
+    sc_out = np.zeros(T * (H // 128), dtype=np.float32)
+    for e in range(off.size - 1):
+        a, b = int(off[e]), int(off[e + 1])
+        n = b - a
+        if n == 0:
+            continue
+        codes = F.unpack_codes(packed[a:b])                      # [n, H]
+        sub = sb[a:b]                                            # [n, H/32]
+        tgt = sub.reshape(n, H // 128, 4).max(axis=2)            # [n, H/128]
+        d = np.repeat(tgt, 4, axis=1) - sub                      # [n, H/32]
+        val = F.e2m1_decode(codes).reshape(n, H // 32, 32) * np.exp2(-d[..., None].astype(np.float64))
+        fp8 = F.e4m3_encode(val.reshape(n, H))                   # [n, H]
+        out[H * a: H * b] = fp8.T.reshape(-1)                    # [H, n]
+        sc = np.exp2(tgt.astype(np.float64) - 127.0).astype(np.float32)  # [n, H/128]
+        sc_out[(H // 128) * a: (H // 128) * b] = sc.T.reshape(-1)
+    return out, sc_out

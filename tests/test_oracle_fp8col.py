@@ -1,0 +1,68 @@
+"""Pins of the MXFP4-row -> FP8-column converter (MoE report, "核心技术贡献"
+items 1-3) -- CPU only."""
+import numpy as np
+import torch
+
+import synth
+from oracle import formats as F
+from oracle import fp8col, mxfp4
+
+
+def test_lossless_when_shift_at_most_8_and_layout():
+    H = 256
+    counts = np.array([3, 0, 5, 1, 0])
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    T = int(off[-1])
+    rng = np.random.default_rng(0)
+    packed = rng.integers(0, 256, size=(T, H // 2), dtype=np.uint8)
+    sb = rng.integers(120, 129, size=(T, H // 32), dtype=np.uint8)   # d <= 8
+    out, sc = fp8col.convert(packed, sb, off, H)
+    codes = F.unpack_codes(packed)
+    for e in range(counts.size):
+        a, n = int(off[e]), int(counts[e])
+        blk = out[H * a: H * (a + n)].reshape(H, n)
+        scl = sc[(H // 128) * a: (H // 128) * (a + n)].reshape(H // 128, n)
+        for t in range(n):
+            for h in range(H):
+                v_in = F.e2m1_decode(codes[a + t, h]) * 2.0 ** (int(sb[a + t, h // 32]) - 127)
+                v_out = F.e4m3_decode(blk[h, t]) * float(scl[h // 128, t])
+                assert v_in == v_out
+                assert (blk[h, t] >> 7) == (codes[a + t, h] >> 3)
+
+
+def test_all_code_shift_pairs_match_torch_rne():
+    # every (code, d) with d = 0..254: value e2m1 * 2**-d rounded to e4m3
+    H = 128
+    rows = []
+    for d in range(255):
+        s = np.zeros(4, np.uint8)
+        s[0] = 254                      # target 254 in sub-block 0
+        s[1] = 254 - d                  # sub-block 1 shifted by d
+        rows.append(s)
+    sb = np.array(rows, np.uint8)
+    T = sb.shape[0]
+    codes = np.tile(np.arange(16, dtype=np.uint8), (T, H // 16))
+    out, _ = fp8col.convert(F.pack_codes(codes), sb, np.array([0, T], np.int64), H)
+    blk = out.reshape(H, T)
+    for d in range(255):
+        vals = F.e2m1_decode(np.arange(16)) * 2.0 ** -d
+        ref = torch.from_numpy(vals.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        got = blk[32:48, d]             # sub-block 1, codes 0..15
+        np.testing.assert_array_equal(got, ref)
+
+
+def test_stepwise_equivalence_on_quantized_activations():
+    counts, off = synth.expert_counts(tokens=300, experts=7, seed=9)
+    x = synth.expert_activations(tokens=300, hidden=384, seed=9)
+    packed, sb = mxfp4.quantize_packed(F.bf16_bits_to_f32(x))
+    out, sc = fp8col.convert(packed, sb, off, 384)
+    # stepwise: FP4 -> float -> (divide by the block target) -> FP8
+    deq = mxfp4.dequantize_f32(F.unpack_codes(packed), sb).astype(np.float64)
+    for e in range(7):
+        a, b = int(off[e]), int(off[e + 1])
+        n = b - a
+        tgt = sb[a:b].reshape(n, 3, 4).max(axis=2).astype(np.float64)
+        scale = np.repeat(np.exp2(tgt - 127), 128, axis=1)
+        ref = torch.from_numpy((deq[a:b] / scale).astype(np.float32)).to(torch.float8_e4m3fn)
+        ref = ref.view(torch.uint8).numpy().T.reshape(-1)
+        np.testing.assert_array_equal(out[384 * a: 384 * b], ref)
