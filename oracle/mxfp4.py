@@ -8,6 +8,7 @@ sharing one UE8M0 scale) for the dispatched activations ("BF16ToFP4Row").
 import numpy as np
 
 from . import formats as F
+from .philox import sr_uniform
 
 BLOCK = 32
 
@@ -27,10 +28,13 @@ def scale_byte(absmax):
     return np.where(a == 0, 0, b).astype(np.uint8)
 
 
-def quantize(x):
+def quantize(x, rounding="rtn", seed=0, step=0, row_ids=None):
     """x: float32 [R, C], C % 32 == 0 -> (codes [R, C], scale bytes [R, C/32]).
 
-    q = x * 2**-e exactly (float64), then E2M1 RTN (saturating at 6)."""
+    q = x * 2**-e exactly (float64), then E2M1 RTN (saturating at 6), or
+    stochastic rounding with the same (seed, step, global index) stream as
+    NVFP4 ("fp4-train", "How it works" describes it for NVFP4; [reading] it
+    applies unchanged to the power-of-two scaled value)."""
     x = np.asarray(x, dtype=np.float32)
     R, C = x.shape
     assert C % BLOCK == 0
@@ -38,12 +42,17 @@ def quantize(x):
     sb = scale_byte(np.max(np.abs(xb), axis=-1))
     e = sb.astype(np.int64) - 127
     q = np.ldexp(xb, -e[..., None])
-    codes = F.e2m1_rtn(q)
+    if rounding == "rtn":
+        codes = F.e2m1_rtn(q)
+    else:
+        rows = np.arange(R, dtype=np.int64) if row_ids is None else np.asarray(row_ids, np.int64)
+        index = (rows[:, None] * C + np.arange(C, dtype=np.int64)[None, :]).reshape(R, C // BLOCK, BLOCK)
+        codes = F.e2m1_sr(q, sr_uniform(index, seed, step))
     return codes.reshape(R, C), sb
 
 
-def quantize_packed(x):
-    codes, sb = quantize(x)
+def quantize_packed(x, rounding="rtn", seed=0, step=0, row_ids=None):
+    codes, sb = quantize(x, rounding, seed, step, row_ids)
     return F.pack_codes(codes), sb
 
 

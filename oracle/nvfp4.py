@@ -64,11 +64,20 @@ def _codes_from_q(x, s_dec, rounding, seed, step, index):
     return F.e2m1_sr(q, u)
 
 
-def quantize(x, st, rounding="rtn", seed=0, step=0):
+def global_index(R, C, row_ids=None):
+    """Global row-major element index of an [R, C] tile whose rows are rows
+    `row_ids` (default 0..R-1) of a tensor with C columns ("fp4-train",
+    "How it works": the SR stream is keyed by the global index)."""
+    rows = np.arange(R, dtype=np.int64) if row_ids is None else np.asarray(row_ids, np.int64)
+    return rows[:, None] * C + np.arange(C, dtype=np.int64)[None, :]
+
+
+def quantize(x, st, rounding="rtn", seed=0, step=0, row_ids=None):
     """x: float32 [R, C] (C % 16 == 0); st: the tensor scale S_t.
 
     Returns (codes uint8 [R, C], scale bytes uint8 [R, C/16]).  SR draws
-    u from Philox keyed by (seed, step, global row-major index)."""
+    u from Philox keyed by (seed, step, global row-major index); row_ids
+    names the tensor rows that x holds when it is a sample of them."""
     x = np.asarray(x, dtype=np.float32)
     R, C = x.shape
     assert C % BLOCK == 0
@@ -76,7 +85,7 @@ def quantize(x, st, rounding="rtn", seed=0, step=0):
     absmax = np.max(np.abs(xb), axis=-1)
     sc = block_scale_codes(absmax, st)
     s_dec = decoded_scale(sc, st)[..., None]
-    index = np.arange(R * C, dtype=np.int64).reshape(R, C // BLOCK, BLOCK)
+    index = global_index(R, C, row_ids).reshape(R, C // BLOCK, BLOCK)
     codes = _codes_from_q(xb, s_dec, rounding, seed, step, index)
     return codes.reshape(R, C), sc
 
@@ -97,12 +106,12 @@ def dequantize(packed, scale_bytes, st, out="bf16"):
     return F.f32_to_bf16_bits(y) if out == "bf16" else y
 
 
-def quantize_packed(x, st, rounding="rtn", seed=0, step=0):
-    codes, sc = quantize(x, st, rounding, seed, step)
+def quantize_packed(x, st, rounding="rtn", seed=0, step=0, row_ids=None):
+    codes, sc = quantize(x, st, rounding, seed, step, row_ids)
     return F.pack_codes(codes), sc
 
 
-def errfeedback_qdq(x, r, st=None, rounding="sr", seed=0, step=0, out="bf16"):
+def errfeedback_qdq(x, r, st=None, rounding="sr", seed=0, step=0, out="bf16", row_ids=None):
     """One error-feedback quantize-dequantize step.
 
     "fp4-train", "How it works" and "Usage": the per-element residual
@@ -116,7 +125,7 @@ def errfeedback_qdq(x, r, st=None, rounding="sr", seed=0, step=0, out="bf16"):
     v = x if r is None else (x + np.asarray(r, dtype=np.float32)).astype(np.float32)
     if st is None:
         st = tensor_scale(v)
-    codes, sc = quantize(v, st, rounding, seed, step)
+    codes, sc = quantize(v, st, rounding, seed, step, row_ids)
     y = dequantize_f32(codes, sc, st)
     if out == "bf16":
         ob = F.f32_to_bf16_bits(y)

@@ -81,3 +81,13 @@ def test_moe_wire_bytes():
     assert f"{fp8_bytes / (M * K):.2f}" == sizes["fp8_bytes_per_mk"][0]
     # a one-byte fp8 scale would print 1.01, a 2-byte MX scale 0.56
     assert f"{(M * K + M * K // 128) / (M * K):.2f}" != sizes["fp8_bytes_per_mk"][0]
+
+
+def test_sr_is_unbiased_at_power_of_two_scale():
+    x = np.full((20000, 32), np.float32(2.3 * 4))      # scale 4: q = 2.3
+    x[:, 0] = np.float32(6.0 * 4)
+    codes, sb = mxfp4.quantize(x, "sr", seed=1, step=2)
+    assert np.all(sb == 129)
+    v = F.e2m1_decode(codes[:, 1:])
+    assert set(np.unique(v)) == {2.0, 3.0}
+    assert abs(v.mean() - 2.3) < 4 * np.sqrt(0.21 / v.size)

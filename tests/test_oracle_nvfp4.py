@@ -117,3 +117,13 @@ def test_zero_scale_block_keeps_sign():
     x[0, 16:] = -1e-30                                      # block scale underflows to 0
     codes, sc = nvfp4.quantize(x, nvfp4.tensor_scale(x))
     assert sc[0, 1] == 0 and np.all(codes[0, 16:] == 8)
+
+
+def test_sampled_rows_use_global_indices():
+    rng = np.random.default_rng(12)
+    x = rng.normal(size=(40, 64)).astype(np.float32)
+    st = nvfp4.tensor_scale(x)
+    full, _ = nvfp4.quantize(x, st, "sr", seed=7, step=3)
+    rows = np.array([0, 5, 39])
+    part, _ = nvfp4.quantize(x[rows], st, "sr", seed=7, step=3, row_ids=rows)
+    np.testing.assert_array_equal(part, full[rows])
