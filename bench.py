@@ -1,0 +1,463 @@
+#!/usr/bin/env python3
+"""Throughput bench of the block-scaled FP4 codec on one MI355X.
+
+Headline step: MXFP4 quantize+pack of a 4096 x 7168 bf16 MoE dispatch
+activation (Student-t(4) * 0.5, 8 hot channels x30) followed by the
+dequantize back to bf16 -- every step of the MXFP4 path (block absmax,
+UE8M0 scale, scaling, E2M1 rounding, packing, receiver).  Inputs are resident
+in HBM; the step rotates over buffer sets whose footprint (> 512 MB) exceeds
+the 256 MB Infinity Cache, so repeats are not served from it.
+
+value = algorithmic bytes per step (every input read once and every output
+written once, both kernels) / measured step time.  Per-kernel durations come
+from HIP events recorded on the launch stream around each launch.
+
+Also reported: a roofline object for the dominant kernel (HBM bound, 8 TB/s
+peak; traffic from the committed rocprofv3 PMC summary when it was taken on
+the current kernel sources), the oracle's throughput on a bounded CPU
+sample, and a breakdown of the other operations of the codec at their own
+workload shapes.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-breakdown]
+                       [--no-cpu-baseline] [--profile-mode {headline,copy}]
+       python bench.py --summarize-trace DIR --out FILE --command CMD
+       python bench.py --summarize-pmc F_HEAD,F_COPY,W_HEAD,W_COPY --out FILE --command CMD
+"""
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+METRIC = "FP4 quantize+pack / dequant throughput, GB/s and % of MI355X HBM peak"
+HBM_PEAK_GBS = 8000.0
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_mxfp4_quantize_4096x7168.txt")
+KERNEL_SOURCES = ["block_scaled_fp4_amd/csrc/quant.hip", "block_scaled_fp4_amd/csrc/device_common.hpp"]
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ timing
+def graph_time(torch, fn, reps, replays=5, check=None):
+    """Mean duration of one fn(k) call: `reps` calls (k = 0..reps-1) are
+    captured in one HIP graph and the graph is replayed `replays` times
+    between HIP events recorded on the launch stream.  Host launch overhead
+    is thus excluded, as it would be for a graph-captured caller.  Falls back
+    to eager launches (events around the loop) if capture is refused."""
+    for k in range(min(reps, 3)):
+        fn(k)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    try:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for k in range(reps):
+                fn(k)
+        g.replay()
+        torch.cuda.synchronize()
+        if check:
+            check()
+        a.record()
+        for _ in range(replays):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / (reps * replays), "graph"
+    except Exception as e:                      # capture unsupported: time eagerly
+        log(f"[bench] graph capture failed ({e}); timing eagerly")
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(replays):
+            for k in range(reps):
+                fn(k)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / (reps * replays), "eager"
+
+
+# --------------------------------------------------------------- headline
+def headline(args, torch, fp4, np, synth):
+    rows, cols = 4096, 7168
+    n = rows * cols
+    q_bytes = 2 * n + n // 2 + n // 32          # read bf16, write codes + UE8M0
+    dq_bytes = n // 2 + n // 32 + 2 * n         # read codes + UE8M0, write bf16
+    log(f"[bench] generating {rows}x{cols} moe_dispatch input")
+    xb = synth.moe_dispatch(rows, cols, seed=2)
+    x0 = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).cuda()
+    nsets = args.sets
+    sets = []
+    for _ in range(nsets):
+        sets.append(dict(x=x0.clone(),
+                         p=torch.empty((rows, cols // 2), dtype=torch.uint8, device="cuda"),
+                         s=torch.empty((rows, cols // 32), dtype=torch.uint8, device="cuda"),
+                         y=torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda")))
+    foot = nsets * (q_bytes + 2 * n)
+    log(f"[bench] {nsets} buffer sets, footprint {foot / 1e6:.0f} MB")
+
+    def quant(k):
+        S = sets[k % nsets]
+        fp4.fp4_quantize(S["x"], "mxfp4", "rtn", packed=S["p"], scales=S["s"])
+
+    def dequant(k):
+        S = sets[k % nsets]
+        fp4.fp4_dequantize(S["p"], S["s"], rows, cols, "mxfp4", y=S["y"])
+
+    def step(k):
+        quant(k)
+        dequant(k)
+
+    if args.profile_mode == "headline":
+        for k in range(args.warmup + args.steps):
+            step(k)
+        torch.cuda.synchronize()
+        log("[bench] profile-mode headline done")
+        return None
+
+    # eager reference outputs of every set, to check the graph replays against
+    for k in range(nsets):
+        step(k)
+    torch.cuda.synchronize()
+    ref = [(S["p"].clone(), S["s"].clone(), S["y"].clone()) for S in sets]
+
+    def check():
+        for S, (p, s, y) in zip(sets, ref):
+            assert torch.equal(S["p"], p) and torch.equal(S["s"], s) and torch.equal(S["y"], y), \
+                "graph replay differs from the eager result"
+
+    reps = args.graph_steps
+    replays = max(1, args.steps // reps)
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    ms_step, mode = graph_time(torch, step, reps, replays, check)
+    q_ms, _ = graph_time(torch, quant, reps, replays)
+    d_ms, _ = graph_time(torch, dequant, reps, replays)
+    check()
+    steps = reps * replays
+    log(f"[bench] {mode}: step {ms_step * 1e3:.2f} us; quantize {q_ms * 1e3:.2f} us; "
+        f"dequantize {d_ms * 1e3:.2f} us ({steps} steps)")
+    return dict(rows=rows, cols=cols, n=n, q_bytes=q_bytes, dq_bytes=dq_bytes, ms_step=ms_step,
+                q_ms=q_ms, d_ms=d_ms, nsets=nsets, footprint=foot, xb=xb, steps=steps, mode=mode)
+
+
+def copy_probe(args, torch):
+    """A plain device copy of known size (PMC calibration for FETCH/WRITE_SIZE)."""
+    nbytes = 256 << 20
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(args.steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"[bench] profile-mode copy: {args.steps} copies of {nbytes} bytes")
+
+
+# ------------------------------------------------------------ breakdown
+def breakdown(args, torch, fp4, np, synth):
+    out = []
+    iters = args.breakdown_iters
+
+    def timed(fn, reps):
+        return graph_time(torch, fn, reps, replays=3)[0]
+
+    def add(op, workload, nbytes, ms, note=None):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        e = dict(op=op, workload=workload, algorithmic_bytes=nbytes, us=round(ms * 1e3, 2),
+                 GBps=round(gbs, 1), frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4))
+        if note:
+            e["note"] = note
+        out.append(e)
+        log(f"[bench] {op:28s} {workload:40s} {ms * 1e3:9.1f} us {gbs:8.1f} GB/s")
+
+    # C1: NVFP4 RTN round trip of a 256 x 2048 bf16 weight block (launch bound)
+    xb = synth.weight_block()
+    x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).cuda()
+    R, C = x.shape
+    n = R * C
+    p = torch.empty((R, C // 2), dtype=torch.uint8, device="cuda")
+    s = torch.empty((R, C // 16), dtype=torch.uint8, device="cuda")
+    ts = torch.empty(1, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    nb = 2 * n + n // 2 + n // 16 + 4
+    add("nvfp4_quantize(rtn,compute)", "256x2048 bf16 weight block", nb,
+        timed(lambda k: fp4.fp4_quantize(x, "nvfp4", "rtn", packed=p, scales=s, tensor_scale=ts), iters),
+        "4 launches: zero, amax, finalize, encode")
+    add("nvfp4_dequantize", "256x2048 bf16 weight block", nb,
+        timed(lambda k: fp4.fp4_dequantize(p, s, R, C, "nvfp4", ts, y=y), iters))
+
+    # C1 shape at 8192 x 8192: the NVFP4 bandwidth row
+    R, C = 8192, 8192
+    n = R * C
+    g = torch.Generator(device="cuda").manual_seed(11)
+    xs = [(torch.randn((R, C), generator=g, device="cuda") * 0.02).to(torch.bfloat16) for _ in range(2)]
+    ps = [torch.empty((R, C // 2), dtype=torch.uint8, device="cuda") for _ in range(2)]
+    ss = [torch.empty((R, C // 16), dtype=torch.uint8, device="cuda") for _ in range(2)]
+    ys = [torch.empty((R, C), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    ts = torch.empty(1, dtype=torch.float32, device="cuda")
+    nb = 2 * n + n // 2 + n // 16
+    fp4.fp4_quantize(xs[0], "nvfp4", "rtn", packed=ps[0], scales=ss[0], tensor_scale=ts)
+    add("nvfp4_quantize(rtn,given)", "8192x8192 bf16", nb,
+        timed(lambda k: fp4.fp4_quantize(xs[k % 2], "nvfp4", "rtn", tscale="given", tensor_scale=ts,
+                                         packed=ps[k % 2], scales=ss[k % 2]), iters))
+    add("nvfp4_quantize(rtn,compute)", "8192x8192 bf16", nb,
+        timed(lambda k: fp4.fp4_quantize(xs[k % 2], "nvfp4", "rtn", tensor_scale=ts,
+                                         packed=ps[k % 2], scales=ss[k % 2]), iters),
+        "includes the amax pass (an extra read of x)")
+    add("nvfp4_dequantize", "8192x8192 bf16", nb,
+        timed(lambda k: fp4.fp4_dequantize(ps[k % 2], ss[k % 2], R, C, "nvfp4", ts, y=ys[k % 2]), iters))
+    add("nvfp4_quantize(sr,given)", "8192x8192 bf16", nb,
+        timed(lambda k: fp4.fp4_quantize(xs[k % 2], "nvfp4", "sr", seed=1, step=k, tscale="given",
+                                         tensor_scale=ts, packed=ps[k % 2], scales=ss[k % 2]), iters))
+    del xs, ps, ss, ys
+
+    # C3: FP4Quant codec on the 8192 x 4096 TP tensor, G = 64 and 256
+    tb = synth.tp_tensor()
+    R, C = tb.shape
+    n = R * C
+    x = torch.from_numpy(tb.view(np.int16)).view(torch.bfloat16).cuda()
+    xs = [x] + [x.clone() for _ in range(3)]
+    for G in (64, 256):
+        pk = [torch.empty((R, C // 2), dtype=torch.uint8, device="cuda") for _ in range(4)]
+        s1 = [torch.empty((R, C // G), dtype=torch.float32, device="cuda") for _ in range(4)]
+        s2 = [torch.empty((R, C // G), dtype=torch.float32, device="cuda") for _ in range(4)]
+        ys = [torch.empty((R, C), dtype=torch.bfloat16, device="cuda") for _ in range(4)]
+        nb = 2 * n + n // 2 + 8 * (n // G)
+        add(f"fp4quant_encode(G={G})", "8192x4096 bf16 TP tensor", nb,
+            timed(lambda k: fp4.fp4quant_encode(xs[k % 4], G, pk[k % 4], s1[k % 4], s2[k % 4]), iters))
+        add(f"fp4quant_decode(G={G})", "8192x4096 bf16 TP tensor", nb,
+            timed(lambda k: fp4.fp4quant_decode(pk[k % 4], s1[k % 4], s2[k % 4], R, C, G, y=ys[k % 4]),
+                  iters))
+    del xs, pk, s1, s2, ys, x
+
+    # C4: SR + error feedback step on an 8192 x 8192 weight (x fp32, r fp32, W bf16)
+    R, C = 8192, 8192
+    n = R * C
+    W = (torch.randn((R, C), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    xf = W.float() + 1e-4 * torch.randn((R, C), generator=g, device="cuda")
+    r = torch.zeros((R, C), dtype=torch.float32, device="cuda")
+    ts = torch.empty(1, dtype=torch.float32, device="cuda")
+    nb = 4 * n + 4 * n + 4 * n + 2 * n
+    add("errfeedback_qdq(sr,compute)", "8192x8192 fp32 x + fp32 r -> bf16 W", nb,
+        timed(lambda k: fp4.fp4_errfeedback_qdq(xf, r, W, None, "sr", 4, k, "compute", ts), max(iters // 2, 5)),
+        "includes the amax pass over x + r (536,870,912 extra bytes read)")
+    add("errfeedback_qdq(sr,given)", "8192x8192 fp32 x + fp32 r -> bf16 W", nb,
+        timed(lambda k: fp4.fp4_errfeedback_qdq(xf, r, W, None, "sr", 4, k, "given", ts), max(iters // 2, 5)))
+    del W, xf, r
+
+    # C5: MXFP4 rows -> FP8 columns over 256 Zipf(1.1) expert shards, 65536 x 7168
+    T, H, E = 65536, 7168, 256
+    counts, off = synth.expert_counts(T, E, seed=5)
+    act = torch.randn((T, H), generator=g, device="cuda").to(torch.bfloat16)
+    pk, sc, _ = fp4.fp4_quantize(act, "mxfp4", "rtn")
+    del act
+    offd = torch.from_numpy(off).cuda()
+    o8 = torch.empty(T * H, dtype=torch.uint8, device="cuda")
+    s8 = torch.empty(T * H // 128, dtype=torch.float32, device="cuda")
+    nb = T * H // 2 + T * H // 32 + T * H + 4 * (T * H // 128)
+    add("mxfp4_row_to_fp8_col", "65536x7168, 256 Zipf(1.1) experts", nb,
+        timed(lambda k: fp4.mxfp4_row_to_fp8_col(pk, sc, offd, H, o8, s8), max(iters // 2, 5)))
+    return out
+
+
+# ---------------------------------------------------------- cpu baseline
+def cpu_baseline(xb, rows_sample):
+    sys.path.insert(0, ROOT)
+    import numpy as np
+    from oracle import formats as F
+    from oracle import mxfp4
+    x = F.bf16_bits_to_f32(xb[:rows_sample])
+    n = x.size
+    t = time.perf_counter()
+    p, s = mxfp4.quantize_packed(x)
+    mxfp4.dequantize(p, s, "bf16")
+    dt = time.perf_counter() - t
+    nbytes = 2 * (2 * n + n // 2 + n // 32)
+    return {"value": round(nbytes / dt / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {rows_sample} of 4096 rows ({n} elements) of the same input, "
+                      f"quantize+dequantize, {dt:.1f} s single-threaded numpy"}
+
+
+# ------------------------------------------------------------ PMC summary
+def read_pmc_summary():
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    kv = {}
+    with open(PMC_SUMMARY) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    return kv
+
+
+def _rocpd_rows(directory, query):
+    """Rows of a query over every rocpd database (rocprofv3 default output) in a directory."""
+    import sqlite3
+    rows = []
+    for fn in sorted(glob.glob(os.path.join(directory, "**", "*.db"), recursive=True)):
+        con = sqlite3.connect(fn)
+        try:
+            rows += con.execute(query).fetchall()
+        finally:
+            con.close()
+    return rows
+
+
+def _short(name):
+    return name.replace("fp4mi::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+
+
+def summarize_trace(directory, out, command):
+    """rocprofv3 --kernel-trace --stats output -> per-kernel duration table."""
+    import statistics
+    per = {}
+    for name, dur in _rocpd_rows(directory, "select name, duration from kernels"):
+        per.setdefault(_short(name), []).append(dur / 1e3)
+    lines = [f"# rocprofv3 kernel trace summary (durations in us)", f"# command: {command}",
+             f"# source_digest: {source_digest()}",
+             f"{'kernel':60s} {'calls':>6s} {'mean':>9s} {'median':>9s} {'min':>9s} {'max':>9s}"]
+    for k, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"{k[:60]:60s} {len(v):6d} {statistics.mean(v):9.2f} {statistics.median(v):9.2f} "
+                     f"{min(v):9.2f} {max(v):9.2f}")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_pmc(dirs, out, command):
+    """Four rocprofv3 --pmc runs (FETCH_SIZE / WRITE_SIZE on the headline and on a
+    plain 256 MiB device copy) -> HBM bytes per launch of the headline kernels,
+    each counter scaled so that the copy reads and writes exactly 256 MiB."""
+    import statistics
+    fh, fc, wh, wc = dirs.split(",")
+    copy_bytes = 256 << 20
+
+    def per_kernel(d, ctr):
+        acc = {}
+        for name, v in _rocpd_rows(d, f"select kernel_name, value from counters_collection "
+                                      f"where counter_name = '{ctr}'"):
+            acc.setdefault(_short(name), []).append(v * 1024.0)
+        return {k: statistics.median(v) for k, v in acc.items()}
+
+    f_copy = per_kernel(fc, "FETCH_SIZE")["__amd_rocclr_copyBuffer"]
+    w_copy = per_kernel(wc, "WRITE_SIZE")["__amd_rocclr_copyBuffer"]
+    kf, kw = copy_bytes / f_copy, copy_bytes / w_copy
+    fetch, write = per_kernel(fh, "FETCH_SIZE"), per_kernel(wh, "WRITE_SIZE")
+    n = 4096 * 7168
+    alg = 2 * n + n // 2 + n // 32
+    q = "quantize_kernel<true, true, false>"
+    d = "dequantize_kernel<true, true>"
+    lines = ["# rocprofv3 PMC summary: HBM traffic of the MXFP4 headline kernels (4096x7168 bf16)",
+             f"# command: {command}",
+             f"# copy calibration: FETCH_SIZE reads {f_copy:.0f} B for a {copy_bytes} B copy (x{kf:.4f}); "
+             f"WRITE_SIZE writes {w_copy:.0f} B (x{kw:.4f})",
+             f"source_digest: {source_digest()}",
+             "kernel: quantize",
+             f"fetch_factor: {kf:.6f}", f"write_factor: {kw:.6f}",
+             f"quantize_fetch_bytes: {fetch[q] * kf:.0f}", f"quantize_write_bytes: {write[q] * kw:.0f}",
+             f"hbm_bytes_per_launch: {fetch[q] * kf + write[q] * kw:.0f}",
+             f"algorithmic_bytes_per_launch: {alg}",
+             f"dequantize_fetch_bytes: {fetch[d] * kf:.0f}", f"dequantize_write_bytes: {write[d] * kw:.0f}",
+             f"dequantize_hbm_bytes_per_launch: {fetch[d] * kf + write[d] * kw:.0f}"]
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--graph-steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--sets", type=int, default=6)
+    ap.add_argument("--breakdown-iters", type=int, default=30)
+    ap.add_argument("--no-breakdown", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--profile-mode", choices=["headline", "copy"])
+    ap.add_argument("--summarize-pmc", help="FETCH_headline,FETCH_copy,WRITE_headline,WRITE_copy dirs")
+    ap.add_argument("--summarize-trace", help="rocprofv3 --kernel-trace output dir")
+    ap.add_argument("--out")
+    ap.add_argument("--command", default="", help="the profiled command, recorded in the summary")
+    args = ap.parse_args()
+
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc, args.out, args.command)
+        return 0
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.out, args.command)
+        return 0
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the codec shards with no exchange (blocks and groups "
+              "are independent), so run it with --gpus 1 and multiply by the GPU count.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    sys.path.insert(0, ROOT)
+    import block_scaled_fp4_amd as fp4
+    import synth
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    if args.profile_mode == "copy":
+        copy_probe(args, torch)
+        return 0
+    h = headline(args, torch, fp4, np, synth)
+    if args.profile_mode:
+        return 0
+    total_bytes = h["q_bytes"] + h["dq_bytes"]
+    value = total_bytes / (h["ms_step"] * 1e-3) / 1e9
+    dom = "quantize" if h["q_ms"] >= h["d_ms"] else "dequantize"
+    dom_ms = max(h["q_ms"], h["d_ms"])
+    dom_bytes = h["q_bytes"] if dom == "quantize" else h["dq_bytes"]
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    traffic = None
+    pmc = read_pmc_summary()
+    if pmc and pmc.get("source_digest") == source_digest() and pmc.get("kernel") == dom:
+        try:
+            traffic = float(pmc["hbm_bytes_per_launch"])
+        except (KeyError, ValueError):
+            traffic = None
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": f"mxfp4 {dom} (4096x7168 bf16)", "algorithmic_bytes_per_launch": dom_bytes}
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": h["steps"], "warmup": args.warmup, "ms_per_step": round(h["ms_step"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "MXFP4 quantize+pack then dequantize of a 4096x7168 bf16 MoE dispatch "
+                               "activation (Student-t(4)*0.5, 8 hot channels x30), RTN, UE8M0 scales",
+                   "rows": h["rows"], "cols": h["cols"], "fmt": "mxfp4", "rounding": "rtn",
+                   "buffer_sets": h["nsets"], "footprint_bytes": h["footprint"]},
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "kernels_us": {"quantize": round(h["q_ms"] * 1e3, 2), "dequantize": round(h["d_ms"] * 1e3, 2)},
+        "timing": f"HIP graph of {args.graph_steps} steps replayed, HIP events on the launch stream ({h['mode']})",
+        "roofline": roof,
+    }
+    if not args.no_breakdown:
+        res["breakdown"] = breakdown(args, torch, fp4, np, synth)
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline: oracle on {args.cpu_rows} rows")
+        res["cpu_baseline"] = cpu_baseline(h["xb"], args.cpu_rows)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

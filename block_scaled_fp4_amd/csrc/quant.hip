@@ -1,0 +1,456 @@
+// NVFP4 / MXFP4 quantize, dequantize and error-feedback qdq for gfx950.
+//
+// "fp4-train" ("How it works", "Usage") and "weight precision part 2"
+// ("Block scaling") define the operations; the MoE report's BF16ToFP4Row is
+// the MXFP4 quantizer.
+//
+// Work decomposition: one thread owns one "octet" of 8 consecutive elements
+// (one 16-byte bf16 load or two 16-byte fp32 loads, one 4-byte store of
+// packed codes).  An NVFP4 block (16) is a lane pair, an MXFP4 block (32) a
+// lane quad; block maxima are combined with DPP quad permutes, so no LDS is
+// used.  Grid-stride loops with strides that are multiples of 256 keep every
+// pair / quad either wholly active or wholly inactive.
+#include "device_common.hpp"
+#include "host_common.hpp"
+
+namespace fp4mi {
+namespace {
+
+// ----------------------------------------------------------- block scales
+struct NvScale {
+  uint32_t code;   // E4M3 byte
+  float sdec;      // fl32(e4m3 * S_t)
+};
+
+// fl32(fl32(absmax / 6) / S_t) -> E4M3 (RNE, saturating); s_dec = fl32(e4m3 * S_t).
+__device__ __forceinline__ NvScale nv_block_scale(float absmax, float st) {
+  float r = absmax / 6.0f;
+  r = r / st;
+  NvScale s;
+  s.code = e4m3_encode_sat(r);
+  s.sdec = e4m3_value(s.code) * st;
+  return s;
+}
+
+// MXFP4: UE8M0 byte = clamp(floor(log2 absmax) - 2 + 127, 0, 254), read from
+// the exponent field; subnormal and zero maxima give 0.
+__device__ __forceinline__ uint32_t mx_scale_byte(float absmax) {
+  int eb = (int)((__float_as_uint(absmax) >> 23) & 0xFFu);
+  return (uint32_t)max(eb - 2, 0);
+}
+
+__device__ __forceinline__ float absmax8(const float (&v)[8]) {
+  float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+  float b = fmaxf(fmaxf(fabsf(v[4]), fabsf(v[5])), fmaxf(fabsf(v[6]), fabsf(v[7])));
+  return fmaxf(a, b);
+}
+
+// Codes of one octet under a decided block scale (software rounding; exact).
+template <bool MX, bool SR>
+__device__ __forceinline__ uint32_t encode_octet_sw(const float (&v)[8], float sdec, int mx_shift,
+                                                    int64_t i, uint64_t seed, uint64_t step) {
+  uint32_t u[8];
+  if constexpr (SR) sr_draws8(i, seed, step, u);
+  uint32_t word = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float q;
+    if constexpr (MX) {
+      q = __builtin_amdgcn_ldexpf(v[j], mx_shift);     // exact unless it lands below 2^-126
+    } else {
+      q = (sdec == 0.0f) ? __builtin_copysignf(0.0f, v[j]) : v[j] / sdec;  // IEEE division
+    }
+    uint32_t c;
+    if constexpr (SR) {
+      // MX: an exactly positive scaled value that underflowed still rounds up when u = 0.
+      bool extra = MX && (q == 0.0f) && (v[j] != 0.0f) && (u[j] == 0u);
+      c = e2m1_sr_mag(fabsf(q), u[j], extra) | sign_nibble(v[j]);
+    } else {
+      c = e2m1_rtn_mag(fabsf(q)) | sign_nibble(v[j]);
+    }
+    word |= c << (4 * j);
+  }
+  return word;
+}
+
+// NVFP4 RTN codes of fl32(v / sdec) without a per-element division.
+// q0 = v * fl32(1/sdec) is within 2^-22 relative of fl32(v / sdec); RTN is
+// monotone in |q|, so when q0 * (1 - 2^-20) and q0 * (1 + 2^-20) round to
+// the same code, so does fl32(v / sdec).  Otherwise (an element within
+// ~2^-20 of a rounding threshold, about 1e-5 of them) the octet is redone
+// with IEEE divisions.  Blocks whose reciprocal is not a normal number go
+// straight to the division path.
+__device__ __forceinline__ uint32_t encode_octet_nv_rtn(const float (&v)[8], float sdec, int64_t i) {
+  const float r = 1.0f / sdec;
+  if (r >= 0x1p-126f && r < 0x1p+127f) {          // a normal reciprocal: the 2^-22 bound holds
+    float lo[8], hi[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float q0 = v[j] * r;
+      lo[j] = q0 * 0x1.fffffp-1f;        // 1 - 2^-20
+      hi[j] = q0 * 0x1.00001p+0f;        // 1 + 2^-20
+    }
+    uint32_t wl = rtn8_unit(lo), wh = rtn8_unit(hi);
+    if (wl == wh) return wl;
+  }
+  return encode_octet_sw<false, false>(v, sdec, 0, i, 0, 0);
+}
+
+// MXFP4 RTN codes: divide by 2^e and round in the converter (bf16 words go
+// in unexpanded; fp32 values are scaled exactly first and converted at unit
+// scale).
+template <bool BF16>
+__device__ __forceinline__ uint32_t encode_octet_mx_rtn(const u32x4& raw, const float (&v)[8],
+                                                        uint32_t sbyte) {
+  if constexpr (BF16) {
+    const float scale = __builtin_amdgcn_ldexpf(1.0f, (int)sbyte - 127);
+    uint32_t w = cvt_fp4x2_bf16<0>(0u, raw.x, scale);
+    w = cvt_fp4x2_bf16<1>(w, raw.y, scale);
+    w = cvt_fp4x2_bf16<2>(w, raw.z, scale);
+    return cvt_fp4x2_bf16<3>(w, raw.w, scale);
+  } else {
+    float q[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) q[j] = __builtin_amdgcn_ldexpf(v[j], 127 - (int)sbyte);
+    return rtn8_unit(q);
+  }
+}
+
+// ------------------------------------------------------------- quantize
+template <bool BF16, bool MX, bool SR>
+__global__ __launch_bounds__(kThreads) void quantize_kernel(
+    const void* __restrict__ x, int64_t n_oct, const float* __restrict__ st_ptr, uint64_t seed,
+    uint64_t step, uint32_t* __restrict__ packed, uint8_t* __restrict__ scales) {
+  const float st = MX ? 1.0f : *st_ptr;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_oct; i += stride) {
+    float v[8];
+    u32x4 raw = {0u, 0u, 0u, 0u};
+    if constexpr (BF16) {
+      raw = ld_u32x4(static_cast<const uint8_t*>(x) + i * 16);
+      v[0] = bf16_lo(raw.x); v[1] = bf16_hi(raw.x); v[2] = bf16_lo(raw.y); v[3] = bf16_hi(raw.y);
+      v[4] = bf16_lo(raw.z); v[5] = bf16_hi(raw.z); v[6] = bf16_lo(raw.w); v[7] = bf16_hi(raw.w);
+    } else {
+      load8<false>(x, i, v);
+    }
+    float am = absmax8(v);
+    am = fmaxf(am, lane_xor1(am));
+    if constexpr (MX) am = fmaxf(am, lane_xor2(am));
+    uint32_t scode, word;
+    if constexpr (MX) {
+      scode = mx_scale_byte(am);
+      if constexpr (SR) word = encode_octet_sw<true, true>(v, 0.0f, 127 - (int)scode, i, seed, step);
+      else word = encode_octet_mx_rtn<BF16>(raw, v, scode);
+    } else {
+      NvScale s = nv_block_scale(am, st);
+      scode = s.code;
+      if constexpr (SR) word = encode_octet_sw<false, true>(v, s.sdec, 0, i, seed, step);
+      else word = encode_octet_nv_rtn(v, s.sdec, i);
+    }
+    st_u32(packed + i, word);
+    if ((i & (MX ? 3 : 1)) == 0) scales[i >> (MX ? 2 : 1)] = (uint8_t)scode;
+  }
+}
+
+// ----------------------------------------------------------- dequantize
+template <bool BF16OUT, bool MX>
+__global__ __launch_bounds__(kThreads) void dequantize_kernel(
+    const uint32_t* __restrict__ packed, const uint8_t* __restrict__ scales,
+    const float* __restrict__ st_ptr, int64_t n_oct, void* __restrict__ y) {
+  const float st = MX ? 1.0f : *st_ptr;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_oct; i += stride) {
+    uint32_t w = packed[i];
+    uint32_t b = scales[i >> (MX ? 2 : 1)];
+    float v[8];
+    if constexpr (MX) {
+      if (b - 1u < 254u) {
+        // scale 2^(b-127) is a normal float whose exponent field is b
+        const float scale = __uint_as_float(b << 23);
+        if constexpr (BF16OUT) {
+          u32x4 o;
+          o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+          o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+          o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+          o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+          st_u32x4(static_cast<uint8_t*>(y) + i * 16, o);
+        } else {
+          typedef float f32x2 __attribute__((ext_vector_type(2)));
+          f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 0);
+          f32x2 bb = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 1);
+          f32x2 c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 2);
+          f32x2 d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 3);
+          v[0] = a.x; v[1] = a.y; v[2] = bb.x; v[3] = bb.y;
+          v[4] = c.x; v[5] = c.y; v[6] = d.x; v[7] = d.y;
+          store8<false>(y, i, v);
+        }
+        continue;
+      }
+      int k = (int)b - 127;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float e = e2m1_value((w >> (4 * j)) & 15u);
+        v[j] = (b == 255u) ? __builtin_nanf("") : __builtin_amdgcn_ldexpf(e, k);
+      }
+    } else {
+      float sdec = e4m3_value_signed(b) * st;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = e2m1_value((w >> (4 * j)) & 15u) * sdec;
+    }
+    store8<BF16OUT>(y, i, v);
+  }
+}
+
+// --------------------------------------------------- tensor amax (NVFP4)
+__global__ void zero_u32_kernel(uint32_t* p) { *p = 0u; }
+
+// max |x (+ r)| over the tensor into *out_bits (atomic max on the bit pattern
+// of a non-negative float, which orders like the value).
+template <bool BF16, bool RES>
+__global__ __launch_bounds__(kThreads) void amax_kernel(const void* __restrict__ x,
+                                                        const float* __restrict__ r, int64_t n_oct,
+                                                        uint32_t* __restrict__ out_bits) {
+  float m = 0.0f;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_oct; i += stride) {
+    float v[8];
+    load8<BF16>(x, i, v);
+    if constexpr (RES) {
+      float rr[8];
+      load8<false>(r, i, rr);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = v[j] + rr[j];
+    }
+    m = fmaxf(m, absmax8(v));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) atomicMax(out_bits, __float_as_uint(m));
+}
+
+// S_t = fl32(A / 2688), 1 when that is 0; written over the amax in place.
+__global__ void tensor_scale_finalize_kernel(float* ts) {
+  float a = __uint_as_float(*reinterpret_cast<uint32_t*>(ts));
+  float s = a / 2688.0f;
+  *ts = (s == 0.0f) ? 1.0f : s;
+}
+
+// ------------------------------------------------- error-feedback qdq
+template <bool BF16IN, bool BF16OUT, bool RES, bool SR, bool CODES>
+__global__ __launch_bounds__(kThreads) void ef_qdq_kernel(
+    const void* x, float* __restrict__ res, void* y, int64_t n_oct,
+    const float* __restrict__ st_ptr, uint64_t seed, uint64_t step, uint32_t* __restrict__ packed,
+    uint8_t* __restrict__ scales) {
+  const float st = *st_ptr;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_oct; i += stride) {
+    float v[8];
+    load8<BF16IN>(x, i, v);
+    if constexpr (RES) {
+      float rr[8];
+      load8<false>(res, i, rr);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = v[j] + rr[j];
+    }
+    float am = absmax8(v);
+    am = fmaxf(am, lane_xor1(am));
+    NvScale s = nv_block_scale(am, st);
+    uint32_t word;
+    if constexpr (SR) word = encode_octet_sw<false, true>(v, s.sdec, 0, i, seed, step);
+    else word = encode_octet_nv_rtn(v, s.sdec, i);
+    float o[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float yv = e2m1_value((word >> (4 * j)) & 15u) * s.sdec;
+      o[j] = BF16OUT ? __uint_as_float(f32_to_bf16_rne(yv) << 16) : yv;
+    }
+    store8<BF16OUT>(y, i, o);
+    if constexpr (RES) {
+      float rn[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) rn[j] = v[j] - o[j];
+      store8<false>(res, i, rn);
+    }
+    if constexpr (CODES) {
+      st_u32(packed + i, word);
+      if ((i & 1) == 0) scales[i >> 1] = (uint8_t)s.code;
+    }
+  }
+}
+
+// ------------------------------------------------------------ launchers
+int launch_tensor_scale(const void* x, bool bf16, const float* res, int64_t n_oct, float* ts,
+                        hipStream_t st) {
+  hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(1), 0, st, reinterpret_cast<uint32_t*>(ts));
+  unsigned g = grid_for(n_oct, 256 * 8);
+  uint32_t* bits = reinterpret_cast<uint32_t*>(ts);
+  if (bf16) {
+    if (res) hipLaunchKernelGGL((amax_kernel<true, true>), dim3(g), dim3(kThreads), 0, st, x, res, n_oct, bits);
+    else     hipLaunchKernelGGL((amax_kernel<true, false>), dim3(g), dim3(kThreads), 0, st, x, res, n_oct, bits);
+  } else {
+    if (res) hipLaunchKernelGGL((amax_kernel<false, true>), dim3(g), dim3(kThreads), 0, st, x, res, n_oct, bits);
+    else     hipLaunchKernelGGL((amax_kernel<false, false>), dim3(g), dim3(kThreads), 0, st, x, res, n_oct, bits);
+  }
+  hipLaunchKernelGGL(tensor_scale_finalize_kernel, dim3(1), dim3(1), 0, st, ts);
+  return launch_status();
+}
+
+template <bool BF16, bool MX>
+void launch_quantize_t(bool sr, const void* x, int64_t n_oct, const float* ts, uint64_t seed,
+                       uint64_t step, uint32_t* packed, uint8_t* scales, hipStream_t st) {
+  unsigned g = grid_for(n_oct);
+  if (sr)
+    hipLaunchKernelGGL((quantize_kernel<BF16, MX, true>), dim3(g), dim3(kThreads), 0, st, x, n_oct,
+                       ts, seed, step, packed, scales);
+  else
+    hipLaunchKernelGGL((quantize_kernel<BF16, MX, false>), dim3(g), dim3(kThreads), 0, st, x,
+                       n_oct, ts, seed, step, packed, scales);
+}
+
+template <bool BF16IN, bool BF16OUT>
+void launch_ef_t(bool res, bool sr, bool codes, const void* x, float* r, void* y, int64_t n_oct,
+                 const float* ts, uint64_t seed, uint64_t step, uint32_t* packed, uint8_t* scales,
+                 hipStream_t st) {
+  unsigned g = grid_for(n_oct);
+#define FP4MI_EF(RES, SR, CODES)                                                                 \
+  hipLaunchKernelGGL((ef_qdq_kernel<BF16IN, BF16OUT, RES, SR, CODES>), dim3(g), dim3(kThreads), \
+                     0, st, x, r, y, n_oct, ts, seed, step, packed, scales)
+  if (res) {
+    if (sr) { if (codes) FP4MI_EF(true, true, true); else FP4MI_EF(true, true, false); }
+    else    { if (codes) FP4MI_EF(true, false, true); else FP4MI_EF(true, false, false); }
+  } else {
+    if (sr) { if (codes) FP4MI_EF(false, true, true); else FP4MI_EF(false, true, false); }
+    else    { if (codes) FP4MI_EF(false, false, true); else FP4MI_EF(false, false, false); }
+  }
+#undef FP4MI_EF
+}
+
+}  // namespace
+}  // namespace fp4mi
+
+using namespace fp4mi;
+
+extern "C" int fp4_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int fmt,
+                            int rounding, uint64_t seed, uint64_t step, int tscale_mode,
+                            float* tensor_scale, uint8_t* packed, uint8_t* scales, void* stream) {
+  int es = dtype_size(dtype);
+  if (!es) return FP4_EDTYPE;
+  if (fmt != FP4_FMT_NVFP4 && fmt != FP4_FMT_MXFP4) return FP4_EINVAL;
+  if (rounding != FP4_ROUND_RTN && rounding != FP4_ROUND_SR) return FP4_EINVAL;
+  const bool mx = fmt == FP4_FMT_MXFP4;
+  if (!mx && tscale_mode != FP4_TSCALE_COMPUTE && tscale_mode != FP4_TSCALE_GIVEN) return FP4_EINVAL;
+  int64_t n;
+  if (!checked_count(rows, cols, &n)) return FP4_ESHAPE;
+  const int blk = mx ? 32 : 16;
+  if (cols % blk) return FP4_ESHAPE;
+  if (n == 0) return FP4_OK;
+  if (!x || !packed || !scales || (!mx && !tensor_scale)) return FP4_EINVAL;
+  if (!is_aligned(x, 16) || !is_aligned(packed, 4) || (!mx && !is_aligned(tensor_scale, 4)))
+    return FP4_EALIGN;
+  const int64_t xb = n * es, pb = n / 2, sb = n / blk;
+  if (overlaps(packed, pb, x, xb) || overlaps(scales, sb, x, xb) || overlaps(packed, pb, scales, sb))
+    return FP4_EOVERLAP;
+  if (!mx && (overlaps(tensor_scale, 4, x, xb) || overlaps(tensor_scale, 4, packed, pb) ||
+              overlaps(tensor_scale, 4, scales, sb)))
+    return FP4_EOVERLAP;
+  hipStream_t st = as_stream(stream);
+  const bool bf16 = dtype == FP4_DTYPE_BF16, sr = rounding == FP4_ROUND_SR;
+  const int64_t n_oct = n / 8;
+  if (!mx && tscale_mode == FP4_TSCALE_COMPUTE) {
+    int rc = launch_tensor_scale(x, bf16, nullptr, n_oct, tensor_scale, st);
+    if (rc) return rc;
+  }
+  uint32_t* pk = reinterpret_cast<uint32_t*>(packed);
+  if (bf16) {
+    if (mx) launch_quantize_t<true, true>(sr, x, n_oct, tensor_scale, seed, step, pk, scales, st);
+    else    launch_quantize_t<true, false>(sr, x, n_oct, tensor_scale, seed, step, pk, scales, st);
+  } else {
+    if (mx) launch_quantize_t<false, true>(sr, x, n_oct, tensor_scale, seed, step, pk, scales, st);
+    else    launch_quantize_t<false, false>(sr, x, n_oct, tensor_scale, seed, step, pk, scales, st);
+  }
+  return launch_status();
+}
+
+extern "C" int fp4_dequantize(const uint8_t* packed, const uint8_t* scales,
+                              const float* tensor_scale, int64_t rows, int64_t cols, int fmt,
+                              void* y, int out_dtype, void* stream) {
+  int es = dtype_size(out_dtype);
+  if (!es) return FP4_EDTYPE;
+  if (fmt != FP4_FMT_NVFP4 && fmt != FP4_FMT_MXFP4) return FP4_EINVAL;
+  const bool mx = fmt == FP4_FMT_MXFP4;
+  int64_t n;
+  if (!checked_count(rows, cols, &n)) return FP4_ESHAPE;
+  const int blk = mx ? 32 : 16;
+  if (cols % blk) return FP4_ESHAPE;
+  if (n == 0) return FP4_OK;
+  if (!packed || !scales || !y || (!mx && !tensor_scale)) return FP4_EINVAL;
+  if (!is_aligned(y, 16) || !is_aligned(packed, 4) || (!mx && !is_aligned(tensor_scale, 4)))
+    return FP4_EALIGN;
+  const int64_t yb = n * es;
+  if (overlaps(y, yb, packed, n / 2) || overlaps(y, yb, scales, n / blk) ||
+      (!mx && overlaps(y, yb, tensor_scale, 4)))
+    return FP4_EOVERLAP;
+  hipStream_t st = as_stream(stream);
+  const int64_t n_oct = n / 8;
+  unsigned g = grid_for(n_oct);
+  const uint32_t* pk = reinterpret_cast<const uint32_t*>(packed);
+  if (out_dtype == FP4_DTYPE_BF16) {
+    if (mx) hipLaunchKernelGGL((dequantize_kernel<true, true>), dim3(g), dim3(kThreads), 0, st, pk, scales, tensor_scale, n_oct, y);
+    else    hipLaunchKernelGGL((dequantize_kernel<true, false>), dim3(g), dim3(kThreads), 0, st, pk, scales, tensor_scale, n_oct, y);
+  } else {
+    if (mx) hipLaunchKernelGGL((dequantize_kernel<false, true>), dim3(g), dim3(kThreads), 0, st, pk, scales, tensor_scale, n_oct, y);
+    else    hipLaunchKernelGGL((dequantize_kernel<false, false>), dim3(g), dim3(kThreads), 0, st, pk, scales, tensor_scale, n_oct, y);
+  }
+  return launch_status();
+}
+
+extern "C" int fp4_errfeedback_qdq(const void* x, int dtype, int64_t rows, int64_t cols,
+                                   float* residual, void* y, int out_dtype, int rounding,
+                                   uint64_t seed, uint64_t step, int tscale_mode,
+                                   float* tensor_scale, uint8_t* packed, uint8_t* scales,
+                                   void* stream) {
+  int es = dtype_size(dtype), eo = dtype_size(out_dtype);
+  if (!es || !eo) return FP4_EDTYPE;
+  if (rounding != FP4_ROUND_RTN && rounding != FP4_ROUND_SR) return FP4_EINVAL;
+  if (tscale_mode != FP4_TSCALE_COMPUTE && tscale_mode != FP4_TSCALE_GIVEN) return FP4_EINVAL;
+  int64_t n;
+  if (!checked_count(rows, cols, &n)) return FP4_ESHAPE;
+  if (cols % 16) return FP4_ESHAPE;
+  if (n == 0) return FP4_OK;
+  if (!x || !y || !tensor_scale) return FP4_EINVAL;
+  if ((packed == nullptr) != (scales == nullptr)) return FP4_EINVAL;
+  if (!is_aligned(x, 16) || !is_aligned(y, 16) || (residual && !is_aligned(residual, 16)) ||
+      !is_aligned(tensor_scale, 4) || (packed && !is_aligned(packed, 4)))
+    return FP4_EALIGN;
+  const int64_t xb = n * es, yb = n * eo, rb = n * 4, pb = n / 2, sb = n / 16;
+  const bool in_place = (y == x) && (dtype == out_dtype);
+  if (!in_place && overlaps(y, yb, x, xb)) return FP4_EOVERLAP;
+  if (residual && (overlaps(residual, rb, x, xb) || overlaps(residual, rb, y, yb))) return FP4_EOVERLAP;
+  const void* outs[3] = {packed, scales, tensor_scale};
+  const int64_t outn[3] = {pb, sb, 4};
+  for (int k = 0; k < 3; ++k) {
+    if (overlaps(outs[k], outn[k], x, xb) || overlaps(outs[k], outn[k], y, yb) ||
+        (residual && overlaps(outs[k], outn[k], residual, rb)))
+      return FP4_EOVERLAP;
+    for (int l = k + 1; l < 3; ++l)
+      if (overlaps(outs[k], outn[k], outs[l], outn[l])) return FP4_EOVERLAP;
+  }
+  hipStream_t st = as_stream(stream);
+  const bool bf16 = dtype == FP4_DTYPE_BF16, obf16 = out_dtype == FP4_DTYPE_BF16;
+  const bool sr = rounding == FP4_ROUND_SR, codes = packed != nullptr;
+  const int64_t n_oct = n / 8;
+  if (tscale_mode == FP4_TSCALE_COMPUTE) {
+    int rc = launch_tensor_scale(x, bf16, residual, n_oct, tensor_scale, st);
+    if (rc) return rc;
+  }
+  uint32_t* pk = reinterpret_cast<uint32_t*>(packed);
+  const bool res = residual != nullptr;
+  if (bf16) {
+    if (obf16) launch_ef_t<true, true>(res, sr, codes, x, residual, y, n_oct, tensor_scale, seed, step, pk, scales, st);
+    else       launch_ef_t<true, false>(res, sr, codes, x, residual, y, n_oct, tensor_scale, seed, step, pk, scales, st);
+  } else {
+    if (obf16) launch_ef_t<false, true>(res, sr, codes, x, residual, y, n_oct, tensor_scale, seed, step, pk, scales, st);
+    else       launch_ef_t<false, false>(res, sr, codes, x, residual, y, n_oct, tensor_scale, seed, step, pk, scales, st);
+  }
+  return launch_status();
+}

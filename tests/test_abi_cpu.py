@@ -1,0 +1,122 @@
+"""The C-ABI library loads, exports what include/fp4mi.h declares, and its
+host-side validation returns the documented status codes without touching
+a GPU (CPU only)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp4mi.h")
+LIB = os.path.join(ROOT, "block_scaled_fp4_amd", "libfp4mi.so")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return re.findall(r"^(?:int|const char\*)\s+(\w+)\(", src, flags=re.M)
+
+
+def header_constants():
+    src = open(HEADER).read()
+    return {k: int(v) for k, v in re.findall(r"#define\s+(FP4\w*)\s+(\d+)", src)}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libfp4mi.so is not built (python -m block_scaled_fp4_amd.build)")
+    return ctypes.CDLL(LIB)
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) >= {"fp4_quantize", "fp4_dequantize", "fp4quant_encode", "fp4quant_decode",
+                          "fp4_errfeedback_qdq", "mxfp4_row_to_fp8_col", "fp4_status_string",
+                          "fp4_abi_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    c = header_constants()
+    lib.fp4_abi_version.restype = ctypes.c_int
+    assert lib.fp4_abi_version() == c["FP4MI_ABI_VERSION"]
+    lib.fp4_status_string.restype = ctypes.c_char_p
+    for k in ("FP4_OK", "FP4_EINVAL", "FP4_ESHAPE", "FP4_EALIGN", "FP4_EDTYPE", "FP4_EHIP",
+              "FP4_EOVERLAP"):
+        assert lib.fp4_status_string(c[k]) not in (None, b"unknown status")
+    assert lib.fp4_status_string(999) == b"unknown status"
+
+
+def test_binding_names_match_header():
+    import block_scaled_fp4_amd as m
+    for n in declared_functions():
+        if n.startswith("fp4_status") or n == "fp4_abi_version":
+            continue
+        assert callable(getattr(m, n)), n
+
+
+# fake, never-dereferenced device addresses: validation must reject before use
+A = 0x7F0000000000
+P, I, I32, I64, U64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
+
+
+def _q(lib, x=A, dtype=1, rows=4, cols=64, fmt=0, rnd=0, tmode=0, ts=A + (1 << 30),
+       packed=A + (2 << 30), scales=A + (3 << 30)):
+    f = lib.fp4_quantize
+    f.argtypes = [P, I, I64, I64, I, I, U64, U64, I, P, P, P, P]
+    return f(x, dtype, rows, cols, fmt, rnd, 0, 0, tmode, ts, packed, scales, None)
+
+
+def test_quantize_validation(lib):
+    c = header_constants()
+    assert _q(lib, dtype=7) == c["FP4_EDTYPE"]
+    assert _q(lib, fmt=5) == c["FP4_EINVAL"]
+    assert _q(lib, rnd=9) == c["FP4_EINVAL"]
+    assert _q(lib, tmode=3) == c["FP4_EINVAL"]
+    assert _q(lib, cols=24) == c["FP4_ESHAPE"]                  # NVFP4 needs cols % 16
+    assert _q(lib, fmt=1, cols=48) == c["FP4_ESHAPE"]           # MXFP4 needs cols % 32
+    assert _q(lib, rows=-1) == c["FP4_ESHAPE"]
+    assert _q(lib, rows=0) == c["FP4_OK"]                       # empty: no-op
+    assert _q(lib, x=None) == c["FP4_EINVAL"]
+    assert _q(lib, ts=None) == c["FP4_EINVAL"]
+    assert _q(lib, x=A + 8) == c["FP4_EALIGN"]
+    assert _q(lib, packed=A + (2 << 30) + 2) == c["FP4_EALIGN"]
+    assert _q(lib, packed=A + 64) == c["FP4_EOVERLAP"]          # inside x's 512 bytes
+    assert _q(lib, scales=A + (2 << 30) + 16) == c["FP4_EOVERLAP"]
+
+
+def test_other_entry_points_validation(lib):
+    c = header_constants()
+    enc = lib.fp4quant_encode
+    enc.argtypes = [P, I, I64, I64, I32, P, P, P, P]
+    assert enc(A, 1, 4, 256, 48, A + (1 << 30), A + (2 << 30), A + (3 << 30), None) == c["FP4_EINVAL"]
+    assert enc(A, 1, 4, 256, 2048, A + (1 << 30), A + (2 << 30), A + (3 << 30), None) == c["FP4_EINVAL"]
+    assert enc(A, 1, 4, 96, 64, A + (1 << 30), A + (2 << 30), A + (3 << 30), None) == c["FP4_ESHAPE"]
+    assert enc(A, 1, 4, 256, 64, A + (1 << 30), A + (1 << 30), A + (3 << 30), None) == c["FP4_EOVERLAP"]
+    dec = lib.fp4quant_decode
+    dec.argtypes = [P, P, P, I64, I64, I32, P, I, P]
+    assert dec(A, A + 4096, A + 8192, 4, 256, 64, A + (1 << 30), 3, None) == c["FP4_EDTYPE"]
+    assert dec(A, A + 4096, A + 8192, 4, 256, 64, A + 4, 1, None) == c["FP4_EALIGN"]
+    ef = lib.fp4_errfeedback_qdq
+    ef.argtypes = [P, I, I64, I64, P, P, I, I, U64, U64, I, P, P, P, P]
+    # in place on the same dtype is allowed; a different dtype over x is not
+    assert ef(A, 0, 2, 32, A + (1 << 30), A + 64, 0, 0, 0, 0, 0, A + (2 << 30), None, None,
+              None) == c["FP4_EOVERLAP"]
+    assert ef(A, 0, 2, 32, A + (1 << 30), A, 1, 0, 0, 0, 0, A + (2 << 30), None, None,
+              None) == c["FP4_EOVERLAP"]
+    assert ef(A, 0, 2, 32, A + (1 << 30), A, 0, 0, 0, 0, 0, A + (2 << 30), A + (3 << 30), None,
+              None) == c["FP4_EINVAL"]                          # packed without scales
+    assert ef(A, 0, 0, 32, None, A, 0, 0, 0, 0, 0, None, None, None, None) == c["FP4_OK"]
+    cv = lib.mxfp4_row_to_fp8_col
+    cv.argtypes = [P, P, P, I32, I64, I64, P, P, P]
+    assert cv(A, A + (1 << 30), A + (2 << 30), 0, 64, 256, A + (3 << 30), A + (4 << 30), None) == c["FP4_EINVAL"]
+    assert cv(A, A + (1 << 30), A + (2 << 30), 4, 64, 200, A + (3 << 30), A + (4 << 30), None) == c["FP4_ESHAPE"]
+    assert cv(A + 4, A + (1 << 30), A + (2 << 30), 4, 64, 256, A + (3 << 30), A + (4 << 30), None) == c["FP4_EALIGN"]
+    assert cv(A, A + (1 << 30), A + (2 << 30), 4, 64, 256, A + 100, A + (4 << 30), None) == c["FP4_EOVERLAP"]
+    assert cv(A, A + (1 << 30), A + (2 << 30), 4, 0, 256, A + (3 << 30), A + (4 << 30), None) == c["FP4_OK"]
+    dq = lib.fp4_dequantize
+    dq.argtypes = [P, P, P, I64, I64, I, P, I, P]
+    assert dq(A, A + (1 << 30), A + (2 << 30), 4, 64, 0, A + 32, 1, None) == c["FP4_EOVERLAP"]
+    assert dq(A, A + (1 << 30), None, 4, 64, 0, A + (3 << 30), 1, None) == c["FP4_EINVAL"]

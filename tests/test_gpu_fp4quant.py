@@ -1,0 +1,125 @@
+"""GPU parity of fp4quant_encode / fp4quant_decode against the oracle within
+the WHT-path tolerance: < 1e-4 of codes differ, each by at most one step of
+the signed grid (+-0 merged); s1 and s2 within 1e-6 relative; decode of the
+GPU's own codes within 1e-6 of the group's largest reconstructed value."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_util import Guarded, dev_bf16, dev_f32, host, host_bf16, need_gpu
+from oracle import formats as F
+from oracle import fp4quant as Q
+
+pytestmark = pytest.mark.gpu
+
+CODE_FRAC = 1e-4
+SCALE_RTOL = 1e-6
+RECON_RTOL = 1e-6
+
+
+def grid_pos(codes):
+    mag = np.asarray(codes).astype(np.int64) & 7
+    sign = np.where((np.asarray(codes) & 8) != 0, -1, 1)
+    return np.where(mag == 0, 0, sign * mag)
+
+
+def encode_gpu(m, x_dev, G):
+    rows, cols = x_dev.shape
+    gp, g1, g2 = Guarded(rows * cols // 2), Guarded(rows * cols // G * 4), Guarded(rows * cols // G * 4)
+    p, s1, s2 = m.fp4quant_encode(x_dev, G, gp.view(torch.uint8, (rows, cols // 2)),
+                                  g1.view(torch.float32, (rows, cols // G)),
+                                  g2.view(torch.float32, (rows, cols // G)))
+    torch.cuda.synchronize()
+    for g in (gp, g1, g2):
+        g.check()
+    return host(p), host(s1), host(s2)
+
+
+def decode_gpu(m, p, s1, s2, G, out):
+    rows, cols = p.shape[0], p.shape[1] * 2
+    gy = Guarded(rows * cols * (2 if out == torch.bfloat16 else 4))
+    y = m.fp4quant_decode(torch.from_numpy(p).cuda(), dev_f32(s1), dev_f32(s2), rows, cols, G, out,
+                          gy.view(out, (rows, cols)))
+    torch.cuda.synchronize()
+    gy.check()
+    return host_bf16(y) if out == torch.bfloat16 else host(y)
+
+
+def check_encode(p, s1, s2, x32, G):
+    rc, r1, r2 = Q.encode(x32, G)
+    codes = F.unpack_codes(p)
+    d = np.abs(grid_pos(codes) - grid_pos(rc))
+    assert d.max() <= 1
+    assert np.mean(d > 0) < CODE_FRAC, np.mean(d > 0)
+    np.testing.assert_allclose(s1, r1, rtol=SCALE_RTOL, atol=0)
+    np.testing.assert_allclose(s2, r2, rtol=SCALE_RTOL, atol=0)
+    return codes
+
+
+def check_decode(m, p, s1, s2, G):
+    codes = F.unpack_codes(p)
+    ref = Q.decode64(codes, s1, s2, G)                          # oracle on the GPU's own codes
+    rows, cols = ref.shape
+    tol = RECON_RTOL * np.repeat(np.abs(ref).reshape(-1, G).max(axis=1), G).reshape(rows, cols)
+    y = decode_gpu(m, p, s1, s2, G, torch.float32)
+    assert np.all(np.abs(y.astype(np.float64) - ref) <= tol)
+    yb = F.bf16_bits_to_f32(decode_gpu(m, p, s1, s2, G, torch.bfloat16)).astype(np.float64)
+    lo = F.bf16_bits_to_f32(F.f32_to_bf16_bits((ref - tol).astype(np.float32))).astype(np.float64)
+    hi = F.bf16_bits_to_f32(F.f32_to_bf16_bits((ref + tol).astype(np.float32))).astype(np.float64)
+    assert np.all((yb >= np.minimum(lo, hi)) & (yb <= np.maximum(lo, hi)))
+
+
+@pytest.mark.parametrize("G", [64, 256])
+def test_tp_tensor_full_size_sampled_rows(G):
+    """8192 x 4096 bf16, N(0,1) with 1% hot columns: encode the whole tensor,
+    compare 32 sampled rows; decode them back."""
+    m = need_gpu()
+    xb = synth.tp_tensor()
+    R, C = xb.shape
+    p, s1, s2 = encode_gpu(m, dev_bf16(xb), G)
+    rows = np.unique(np.concatenate([[0, R - 1], np.random.default_rng(G).choice(R, 30, replace=False)]))
+    check_encode(p[rows], s1[rows], s2[rows], F.bf16_bits_to_f32(xb[rows]), G)
+    check_decode(m, p[rows], s1[rows], s2[rows], G)
+
+
+@pytest.mark.parametrize("G", [16, 32, 64, 128, 256, 512, 1024])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_all_group_sizes_small(G, dtype):
+    m = need_gpu()
+    rng = np.random.default_rng(G)
+    rows, cols = 37, 2 * 1024
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    x[:, rng.choice(cols, 20, replace=False)] *= 20
+    x[3] = 0.0                                       # zero groups
+    x[4, :G] = 0.0
+    x[4, 7] = -2.5                                   # one-hot group
+    x[5, :G] = 0.375                                 # constant group
+    x[6] *= 2.0 ** -60                               # tiny and huge rows
+    x[7] *= 2.0 ** 40
+    if dtype == "bf16":
+        xb = synth.to_bf16_bits(x)
+        x = F.bf16_bits_to_f32(xb)
+        xd = dev_bf16(xb)
+    else:
+        xd = dev_f32(x)
+    p, s1, s2 = encode_gpu(m, xd, G)
+    codes = check_encode(p, s1, s2, x, G)
+    assert np.all(codes[3] == 0) and np.all(s1[3] == 0) and np.all(s2[3] == 0)
+    assert np.all(np.abs(F.e2m1_decode(codes[4, :G])) == 6.0)
+    check_decode(m, p, s1, s2, G)
+    # closed forms reconstruct exactly (to fp32 rounding of the scales)
+    y = decode_gpu(m, p, s1, s2, G, torch.float32)
+    np.testing.assert_allclose(y[4, :G], x[4, :G], atol=1e-6 * 2.5)
+    np.testing.assert_allclose(y[5, :G], x[5, :G], rtol=1e-6)
+
+
+def test_power_of_two_invariance_on_gpu():
+    m = need_gpu()
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((64, 1024)).astype(np.float32)
+    p, s1, s2 = encode_gpu(m, dev_f32(x), 256)
+    p2, t1, t2 = encode_gpu(m, dev_f32(np.ldexp(x, 13).astype(np.float32)), 256)
+    np.testing.assert_array_equal(p2, p)
+    np.testing.assert_array_equal(t2, s2)
+    np.testing.assert_array_equal(t1, np.ldexp(s1, 13).astype(np.float32))

@@ -1,0 +1,104 @@
+"""GPU parity of mxfp4_row_to_fp8_col against the oracle (bit-exact FP8
+bytes and fp32 scales, ragged expert shards, guard bands)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_util import Guarded, dev_i64, dev_u8, host, need_gpu
+from oracle import formats as F
+from oracle import fp8col, mxfp4
+
+pytestmark = pytest.mark.gpu
+
+
+def convert_gpu(m, packed, sb, off, H):
+    T = packed.shape[0]
+    go, gs = Guarded(T * H), Guarded(T * H // 128 * 4)
+    o, s = m.mxfp4_row_to_fp8_col(dev_u8(packed), dev_u8(sb), dev_i64(off), H,
+                                  go.view(torch.uint8, (T * H,)), gs.view(torch.float32, (T * H // 128,)))
+    torch.cuda.synchronize()
+    go.check()
+    gs.check()
+    return host(o), host(s)
+
+
+@pytest.mark.parametrize("counts,H", [
+    ([3, 0, 5, 1, 0, 64, 130, 0, 7], 384),
+    ([0, 0, 1], 128),
+    ([64, 64, 64], 256),
+    ([200], 7168),
+])
+def test_small_ragged_from_quantized_activations(counts, H):
+    m = need_gpu()
+    counts = np.array(counts)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    T = int(off[-1])
+    x = synth.expert_activations(tokens=T, hidden=H, seed=int(T + H))
+    packed, sb = mxfp4.quantize_packed(F.bf16_bits_to_f32(x))
+    o, s = convert_gpu(m, packed, sb, off, H)
+    ro, rs = fp8col.convert(packed, sb, off, H)
+    np.testing.assert_array_equal(o, ro)
+    np.testing.assert_array_equal(s.view(np.uint32), rs.view(np.uint32))
+
+
+def test_every_code_and_shift():
+    m = need_gpu()
+    H = 128
+    rows = []
+    for d in range(255):
+        r = np.zeros(4, np.uint8)
+        r[0], r[1], r[2], r[3] = 254, 254 - d, 254 - min(d, 3), 200
+        rows.append(r)
+    sb = np.array(rows, np.uint8)
+    T = sb.shape[0]
+    codes = np.tile(np.arange(16, dtype=np.uint8), (T, H // 16))
+    packed = F.pack_codes(codes)
+    off = np.array([0, 100, 100, T], np.int64)
+    o, s = convert_gpu(m, packed, sb, off, H)
+    ro, rs = fp8col.convert(packed, sb, off, H)
+    np.testing.assert_array_equal(o, ro)
+    np.testing.assert_array_equal(s.view(np.uint32), rs.view(np.uint32))
+
+
+def test_many_empty_experts_inside_one_tile():
+    m = need_gpu()
+    H = 256
+    counts = np.zeros(500, np.int64)
+    counts[[3, 100, 101, 250, 499]] = [10, 5, 1, 40, 90]
+    counts[400:470] = 1                                   # 70 one-token experts in one tile
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    T = int(off[-1])
+    packed, sb = synth.random_mxfp4(T, H, seed=3)
+    o, s = convert_gpu(m, packed, sb, off, H)
+    ro, rs = fp8col.convert(packed, sb, off, H)
+    np.testing.assert_array_equal(o, ro)
+    np.testing.assert_array_equal(s.view(np.uint32), rs.view(np.uint32))
+
+
+def test_full_size_zipf_shards_sampled_experts():
+    """65,536 tokens x 7168 in 256 Zipf(1.1) shards, random MXFP4 rows: the
+    whole conversion runs on the GPU; the oracle checks, per sampled expert,
+    every byte of two sampled FP8 block rows (256 channels) and the scales."""
+    m = need_gpu()
+    T, H, E = 65536, 7168, 256
+    counts, off = synth.expert_counts(T, E, seed=5)
+    packed, sb = synth.random_mxfp4(T, H, seed=5, scale_lo=110, scale_hi=140)
+    o, s = convert_gpu(m, packed, sb, off, H)
+    rng = np.random.default_rng(0)
+    experts = np.unique(np.concatenate([[0, 1, E - 1, E - 2], rng.choice(E, 6, replace=False)]))
+    HB = H // 128
+    for e in experts:
+        a, b = int(off[e]), int(off[e + 1])
+        n = b - a
+        if n == 0:
+            continue
+        blocks = np.unique([0, HB - 1, int(rng.integers(HB))])
+        for blk in blocks:
+            cols = slice(blk * 64, blk * 64 + 64)
+            scs = slice(blk * 4, blk * 4 + 4)
+            ro, rs = fp8col.convert(packed[a:b, cols], sb[a:b, scs], np.array([0, n], np.int64), 128)
+            got = o[H * a: H * b].reshape(H, n)[blk * 128: blk * 128 + 128]
+            np.testing.assert_array_equal(got.reshape(-1), ro)
+            gs = s[HB * a: HB * b].reshape(HB, n)[blk]
+            np.testing.assert_array_equal(gs.view(np.uint32), rs.view(np.uint32))
