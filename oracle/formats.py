@@ -129,7 +129,7 @@ E4M3_MAX = 448.0
 def e4m3_encode(x):
     """float -> OCP E4M3FN byte, round-to-nearest-even, saturating at 448.
 
-    [reading] "fp4-train" only says the block scale is "encoded to e4m3" in
+    [reading] "fp4-train" only says the block scale is converted to e4m3 in
     software; IEEE nearest-even with saturation to the largest finite value
     (E4M3FN has no infinity) is taken.  Definition used: the representable
     magnitude at minimum distance, ties to the even code, magnitudes above
