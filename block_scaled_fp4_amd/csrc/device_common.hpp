@@ -38,8 +38,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
   return (f != f) ? ((u >> 16) | 0x40u) : r;
 }
+// Two fp32 -> two bf16 (RNE) with the gfx950 converter (v_cvt_pk_bf16_f32),
+// which agrees with f32_to_bf16_rne on every non-NaN fp32 (checked
+// exhaustively on the GPU); NaN stays NaN with an unspecified payload.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // Load 8 consecutive elements (element index 8*i .. 8*i+7) as fp32.
@@ -142,8 +148,6 @@ __device__ __forceinline__ uint32_t e2m1_sr_mag(float a, uint32_t u24, bool extr
 // (first input in the low nibble).  Checked bit-for-bit against e2m1_rtn on
 // all 2^32 fp32 inputs at scale 1, and on every bf16 input at every scale
 // 2^k, k in [-127, 127]; only those uses appear in this library.
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
 template <int SEL>
 __device__ __forceinline__ uint32_t cvt_fp4x2_f32(uint32_t old, float a, float b, float scale) {
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, scale, SEL);
@@ -153,6 +157,18 @@ __device__ __forceinline__ uint32_t cvt_fp4x2_bf16(uint32_t old, uint32_t two_bf
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(old, __builtin_bit_cast(bf16x2_t, two_bf16),
                                                    scale, SEL);
 }
+// Eight E2M1 codes of a word -> eight fp32 values times a power-of-two
+// scale (v_cvt_scalef32_pk_f32_fp4; exact at every normal power-of-two
+// scale, checked exhaustively on the GPU).
+__device__ __forceinline__ void e2m1x8_to_f32(uint32_t w, float scale, float (&v)[8]) {
+  const f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 0);
+  const f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 1);
+  const f32x2 c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 2);
+  const f32x2 d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 3);
+  v[0] = a.x; v[1] = a.y; v[2] = b.x; v[3] = b.y;
+  v[4] = c.x; v[5] = c.y; v[6] = d.x; v[7] = d.y;
+}
+
 // Eight fp32 values at unit scale -> eight RTN codes in one word.
 __device__ __forceinline__ uint32_t rtn8_unit(const float (&q)[8]) {
   uint32_t w = cvt_fp4x2_f32<0>(0u, q[0], q[1], 1.0f);
@@ -170,13 +186,6 @@ __device__ __forceinline__ float e2m1_value(uint32_t code) {
   return __uint_as_float(__float_as_uint(mag) | ((code & 8u) << 28));
 }
 
-// Twice the E2M1 value as an integer in [-12, 12] (exact).
-__device__ __forceinline__ int e2m1_twice_int(uint32_t code) {
-  uint32_t m3 = code & 7u;
-  int mag = (m3 < 4u) ? (int)m3 : (int)((2u + (m3 & 1u)) << ((m3 >> 1) - 1u));
-  return (code & 8u) ? -mag : mag;
-}
-
 // -------------------------------------------------------------------- E4M3
 // r >= 0 (may be +inf) -> OCP E4M3FN byte, round to nearest even, saturating
 // at 448 (0x7E).
@@ -189,6 +198,14 @@ __device__ __forceinline__ uint32_t e4m3_encode_sat(float r) {
   u += 0x7FFFFu + ((u >> 20) & 1u);                       // RNE to 3 mantissa bits
   uint32_t e = (u >> 23) - 120u;                          // rebias 127 -> 7
   return (e << 3) | ((u >> 20) & 7u);
+}
+
+// The same encoding through the gfx950 fp8 converter: v_cvt_pk_fp8_f32 rounds
+// to nearest even and agrees with e4m3_encode_sat on every non-negative fp32
+// below 464 (checked exhaustively on the GPU); clamping at 448 first makes
+// it saturate like e4m3_encode_sat above that.
+__device__ __forceinline__ uint32_t e4m3_encode_sat_hw(float r) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(r, 448.0f), 0.0f, 0, false) & 0xFFu;
 }
 
 // E4M3FN byte (finite, sign ignored) -> fp32 magnitude.
@@ -210,8 +227,9 @@ __device__ __forceinline__ void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     if (r) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
-    uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
-    uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t lo0 = (uint32_t)p0, hi0 = (uint32_t)(p0 >> 32);
+    const uint32_t lo1 = (uint32_t)p1, hi1 = (uint32_t)(p1 >> 32);
     uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
     c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
   }
@@ -230,6 +248,12 @@ __device__ __forceinline__ void sr_draws8(int64_t i, uint64_t seed, uint64_t ste
     u[4 * h + 0] = c0 >> 8; u[4 * h + 1] = c1 >> 8;
     u[4 * h + 2] = c2 >> 8; u[4 * h + 3] = c3 >> 8;
   }
+}
+
+// Workgroups for an exact grid in which each thread owns `per_thread` items.
+inline int64_t blocks_for(int64_t items, int per_thread) {
+  const int64_t per_block = (int64_t)kThreads * per_thread;
+  return (items + per_block - 1) / per_block;
 }
 
 // Grid size for a grid-stride loop over `items` work items of one thread each.

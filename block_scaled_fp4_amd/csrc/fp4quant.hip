@@ -19,7 +19,7 @@
 // so the codes never depend on s1 and the transform runs on the raw input.
 // Receiver arithmetic.  With c2 = 2 * e2m1(code) (integers in [-12, 12]),
 //   x' = s1 * H(e2m1 * s2) / sqrt(G) = (H c2) * (s1 s2 / (2 sqrt(G))),
-// and H c2 is computed exactly in 32-bit integers.
+// and H c2 is computed exactly (integer-valued fp32 butterflies).
 #include "device_common.hpp"
 #include "host_common.hpp"
 
@@ -32,13 +32,6 @@ __device__ __forceinline__ float xlane(float v) {
   else if constexpr (M == 2) return lane_xor2(v);
   else return __shfl_xor(v, M);
 }
-template <int M>
-__device__ __forceinline__ int xlane_i(int v) {
-  if constexpr (M == 1) return lane_xor1_i(v);
-  else if constexpr (M == 2) return lane_xor2_i(v);
-  else return __shfl_xor(v, M);
-}
-
 // In-register butterflies over the EPL elements of a lane (natural order).
 template <int EPL, typename T>
 __device__ __forceinline__ void wht_local(T (&v)[EPL]) {
@@ -65,15 +58,6 @@ __device__ __forceinline__ void wht_stage(float (&v)[EPL], bool upper) {
     v[j] = upper ? (p - v[j]) : (v[j] + p);
   }
 }
-template <int M, int EPL>
-__device__ __forceinline__ void wht_stage_i(int (&v)[EPL], bool upper) {
-#pragma unroll
-  for (int j = 0; j < EPL; ++j) {
-    int p = xlane_i<M>(v[j]);
-    v[j] = upper ? (p - v[j]) : (v[j] + p);
-  }
-}
-
 template <int LPG, int EPL>
 __device__ __forceinline__ void wht_cross(float (&v)[EPL], int lane) {
   if constexpr (LPG > 1) wht_stage<1, EPL>(v, lane & 1);
@@ -83,16 +67,6 @@ __device__ __forceinline__ void wht_cross(float (&v)[EPL], int lane) {
   if constexpr (LPG > 16) wht_stage<16, EPL>(v, lane & 16);
   if constexpr (LPG > 32) wht_stage<32, EPL>(v, lane & 32);
 }
-template <int LPG, int EPL>
-__device__ __forceinline__ void wht_cross_i(int (&v)[EPL], int lane) {
-  if constexpr (LPG > 1) wht_stage_i<1, EPL>(v, lane & 1);
-  if constexpr (LPG > 2) wht_stage_i<2, EPL>(v, lane & 2);
-  if constexpr (LPG > 4) wht_stage_i<4, EPL>(v, lane & 4);
-  if constexpr (LPG > 8) wht_stage_i<8, EPL>(v, lane & 8);
-  if constexpr (LPG > 16) wht_stage_i<16, EPL>(v, lane & 16);
-  if constexpr (LPG > 32) wht_stage_i<32, EPL>(v, lane & 32);
-}
-
 // Butterfly (pairwise) reductions across the LPG lanes of a group.
 template <int LPG>
 __device__ __forceinline__ float group_sum(float s) {
@@ -128,45 +102,68 @@ __device__ __forceinline__ float sumsq(const float (&v)[EPL]) {
   return t[0];
 }
 
+// Per-group encode of the EPL elements a lane holds (all lanes of the wave
+// take part: the cross-lane stages need every lane of the group).
+template <int EPL, int LPG>
+__device__ __forceinline__ void encode_lane(float (&v)[EPL], int lane, float inv_g, float c_s2,
+                                            uint32_t (&words)[EPL / 8], float* s1o, float* s2o) {
+  const float ss = group_sum<LPG>(sumsq<EPL>(v));
+  wht_local<EPL>(v);
+  wht_cross<LPG, EPL>(v, lane);
+  float mx = 0.0f;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) mx = fmaxf(mx, fabsf(v[j]));
+  mx = group_max<LPG>(mx);
+  const bool zero = (ss == 0.0f) || (mx == 0.0f);
+  const float s1 = __builtin_sqrtf(ss * inv_g);
+  const float rq = zero ? 0.0f : 6.0f / mx;
+#pragma unroll
+  for (int k = 0; k < EPL / 8; ++k) {
+    float q[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) q[j] = v[8 * k + j] * rq;     // +-0 when zero: code 0 or 8
+    words[k] = zero ? 0u : rtn8_unit(q);
+  }
+  *s1o = zero ? 0.0f : s1;
+  *s2o = zero ? 0.0f : (mx * c_s2) / s1;
+}
+
+// Thread t of workgroup b owns lane-items b*256*U + t + 256*k (k < U); each
+// lane-item is EPL consecutive elements, LPG consecutive lane-items a group.
 template <bool BF16, int EPL, int LPG>
 __global__ __launch_bounds__(kThreads) void fp4quant_encode_kernel(
     const void* __restrict__ x, int64_t n_lane, float inv_g, float c_s2,
     uint32_t* __restrict__ packed, float* __restrict__ s_rms, float* __restrict__ s_abs) {
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  constexpr int U = (EPL == 8) ? 2 : 1;
+  constexpr int OCT = EPL / 8;
   const int lane = threadIdx.x & 63;
-  for (int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x; t < n_lane; t += stride) {
-    float v[EPL];
+  const int64_t base = (int64_t)blockIdx.x * (kThreads * U) + threadIdx.x;
+  float v[U][EPL];
 #pragma unroll
-    for (int k = 0; k < EPL / 8; ++k) {
-      float o[8];
-      load8<BF16>(x, t * (EPL / 8) + k, o);
+  for (int k = 0; k < U; ++k) {
+    const int64_t t = base + (int64_t)k * kThreads;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[8 * k + j] = o[j];
+    for (int o = 0; o < OCT; ++o) {
+      float e[8];
+      if (t < n_lane) load8<BF16>(x, t * OCT + o, e);
+      else for (int j = 0; j < 8; ++j) e[j] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[k][8 * o + j] = e[j];
     }
-    const float ss = group_sum<LPG>(sumsq<EPL>(v));
-    wht_local<EPL>(v);
-    wht_cross<LPG, EPL>(v, lane);
-    float mx = 0.0f;
+  }
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) mx = fmaxf(mx, fabsf(v[j]));
-    mx = group_max<LPG>(mx);
-    const bool zero = (ss == 0.0f) || (mx == 0.0f);
-    const float s1 = __builtin_sqrtf(ss * inv_g);
-    const float rq = zero ? 0.0f : 6.0f / mx;
+  for (int k = 0; k < U; ++k) {
+    const int64_t t = base + (int64_t)k * kThreads;
+    uint32_t words[OCT];
+    float s1, s2;
+    encode_lane<EPL, LPG>(v[k], lane, inv_g, c_s2, words, &s1, &s2);
+    if (t < n_lane) {
 #pragma unroll
-    for (int k = 0; k < EPL / 8; ++k) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        uint32_t c = zero ? 0u : e2m1_rtn(v[8 * k + j] * rq);
-        word |= c << (4 * j);
+      for (int o = 0; o < OCT; ++o) st_u32(packed + t * OCT + o, words[o]);
+      if ((lane & (LPG - 1)) == 0) {
+        s_rms[t / LPG] = s1;
+        s_abs[t / LPG] = s2;
       }
-      st_u32(packed + t * (EPL / 8) + k, word);
-    }
-    if ((lane & (LPG - 1)) == 0) {
-      const int64_t g = t / LPG;
-      s_rms[g] = zero ? 0.0f : s1;
-      s_abs[g] = zero ? 0.0f : (mx * c_s2) / s1;
     }
   }
 }
@@ -175,26 +172,42 @@ template <bool BF16OUT, int EPL, int LPG>
 __global__ __launch_bounds__(kThreads) void fp4quant_decode_kernel(
     const uint32_t* __restrict__ packed, const float* __restrict__ s_rms,
     const float* __restrict__ s_abs, int64_t n_lane, float c_dec, void* __restrict__ y) {
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  constexpr int U = (EPL == 8) ? 2 : 1;
+  constexpr int OCT = EPL / 8;
   const int lane = threadIdx.x & 63;
-  for (int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x; t < n_lane; t += stride) {
-    const int64_t g = t / LPG;
-    const float f = (s_rms[g] * s_abs[g]) * c_dec;
-    int c[EPL];
+  const int64_t base = (int64_t)blockIdx.x * (kThreads * U) + threadIdx.x;
+  uint32_t w[U][OCT];
+  float f[U];
+  // 2 * e2m1 values are integers in [-12, 12]; every partial sum of the
+  // transform is an integer below 2^14, so fp32 butterflies on them are exact.
 #pragma unroll
-    for (int k = 0; k < EPL / 8; ++k) {
-      uint32_t w = packed[t * (EPL / 8) + k];
+  for (int k = 0; k < U; ++k) {
+    const int64_t t = base + (int64_t)k * kThreads;
+    const bool ok = t < n_lane;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) c[8 * k + j] = e2m1_twice_int((w >> (4 * j)) & 15u);
+    for (int o = 0; o < OCT; ++o) w[k][o] = ok ? __builtin_nontemporal_load(packed + t * OCT + o) : 0u;
+    f[k] = ok ? (s_rms[t / LPG] * s_abs[t / LPG]) * c_dec : 0.0f;
+  }
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+    const int64_t t = base + (int64_t)k * kThreads;
+    float c[EPL];
+#pragma unroll
+    for (int o = 0; o < OCT; ++o) {
+      float e[8];
+      e2m1x8_to_f32(w[k][o], 2.0f, e);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) c[8 * o + j] = e[j];
     }
     wht_local<EPL>(c);
-    wht_cross_i<LPG, EPL>(c, lane);
+    wht_cross<LPG, EPL>(c, lane);
+    if (t >= n_lane) continue;
 #pragma unroll
-    for (int k = 0; k < EPL / 8; ++k) {
-      float o[8];
+    for (int o = 0; o < OCT; ++o) {
+      float out[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) o[j] = (float)c[8 * k + j] * f;
-      store8<BF16OUT>(y, t * (EPL / 8) + k, o);
+      for (int j = 0; j < 8; ++j) out[j] = c[8 * o + j] * f[k];
+      store8<BF16OUT>(y, t * OCT + o, out);
     }
   }
 }
@@ -207,7 +220,8 @@ void launch_encode(int G, const void* x, int64_t n, uint32_t* pk, float* s1, flo
 #define FP4MI_ENC(EPL, LPG)                                                                   \
   {                                                                                           \
     int64_t nl = n / EPL;                                                                     \
-    hipLaunchKernelGGL((fp4quant_encode_kernel<BF16, EPL, LPG>), dim3(grid_for(nl)),         \
+    hipLaunchKernelGGL((fp4quant_encode_kernel<BF16, EPL, LPG>),                              \
+                       dim3((unsigned)blocks_for(nl, EPL == 8 ? 2 : 1)),                      \
                        dim3(kThreads), 0, st, x, nl, inv_g, c_s2, pk, s1, s2);                 \
   }
   switch (G) {
@@ -229,7 +243,8 @@ void launch_decode(int G, const uint32_t* pk, const float* s1, const float* s2, 
 #define FP4MI_DEC(EPL, LPG)                                                                   \
   {                                                                                           \
     int64_t nl = n / EPL;                                                                     \
-    hipLaunchKernelGGL((fp4quant_decode_kernel<BF16OUT, EPL, LPG>), dim3(grid_for(nl)),      \
+    hipLaunchKernelGGL((fp4quant_decode_kernel<BF16OUT, EPL, LPG>),                           \
+                       dim3((unsigned)blocks_for(nl, EPL == 8 ? 2 : 1)),                      \
                        dim3(kThreads), 0, st, pk, s1, s2, nl, c_dec, y);                      \
   }
   switch (G) {
@@ -268,6 +283,7 @@ extern "C" int fp4quant_encode(const void* x, int dtype, int64_t rows, int64_t c
       overlaps(packed, pb, s_rms, gb) || overlaps(packed, pb, s_abs, gb) ||
       overlaps(s_rms, gb, s_abs, gb))
     return FP4_EOVERLAP;
+  if (blocks_for(n / 8, 1) > 0x7FFFFFFF) return FP4_ESHAPE;
   hipStream_t st = as_stream(stream);
   uint32_t* pk = reinterpret_cast<uint32_t*>(packed);
   if (dtype == FP4_DTYPE_BF16) launch_encode<true>(group, x, n, pk, s_rms, s_abs, st);
@@ -291,6 +307,7 @@ extern "C" int fp4quant_decode(const uint8_t* packed, const float* s_rms, const 
   const int64_t yb = n * es, gb = (n / group) * 4;
   if (overlaps(y, yb, packed, n / 2) || overlaps(y, yb, s_rms, gb) || overlaps(y, yb, s_abs, gb))
     return FP4_EOVERLAP;
+  if (blocks_for(n / 8, 1) > 0x7FFFFFFF) return FP4_ESHAPE;
   hipStream_t st = as_stream(stream);
   const uint32_t* pk = reinterpret_cast<const uint32_t*>(packed);
   if (out_dtype == FP4_DTYPE_BF16) launch_decode<true>(group, pk, s_rms, s_abs, n, y, st);

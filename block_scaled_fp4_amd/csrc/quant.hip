@@ -16,6 +16,10 @@
 namespace fp4mi {
 namespace {
 
+// Octets per thread: enough independent 16-byte loads in flight per lane to
+// cover HBM latency (64 bytes of input per thread for either dtype).
+template <bool BF16> constexpr int kOctets = BF16 ? 4 : 2;
+
 // ----------------------------------------------------------- block scales
 struct NvScale {
   uint32_t code;   // E4M3 byte
@@ -23,13 +27,40 @@ struct NvScale {
 };
 
 // fl32(fl32(absmax / 6) / S_t) -> E4M3 (RNE, saturating); s_dec = fl32(e4m3 * S_t).
-__device__ __forceinline__ NvScale nv_block_scale(float absmax, float st) {
+__device__ __forceinline__ NvScale nv_block_scale_exact(float absmax, float st) {
   float r = absmax / 6.0f;
   r = r / st;
   NvScale s;
-  s.code = e4m3_encode_sat(r);
+  s.code = e4m3_encode_sat_hw(r);
   s.sdec = e4m3_value(s.code) * st;
   return s;
+}
+
+// The same scale without the two divisions.  With kinv = fl32(1/fl32(6 S_t))
+// a normal number, r' = absmax * kinv is within 2^-21 (relative) of
+// fl32(fl32(absmax/6)/S_t); E4M3 encoding is monotone, so if r'(1 - 2^-18)
+// and r'(1 + 2^-18) encode to the same byte the exact quotient does too.
+// Otherwise (a quotient within 2^-18 of an E4M3 rounding boundary) the
+// divisions are done.
+__device__ __forceinline__ NvScale nv_block_scale(float absmax, float st, float kinv, bool fast) {
+  if (fast) {
+    const float r = absmax * kinv;
+    const uint32_t lo = e4m3_encode_sat_hw(r * 0x1.fffcp-1f);     // 1 - 2^-18
+    const uint32_t hi = e4m3_encode_sat_hw(r * 0x1.00004p+0f);    // 1 + 2^-18
+    if (lo == hi) {
+      NvScale s;
+      s.code = lo;
+      s.sdec = e4m3_value(lo) * st;
+      return s;
+    }
+  }
+  return nv_block_scale_exact(absmax, st);
+}
+
+__device__ __forceinline__ float nv_kinv(float st, bool* fast) {
+  const float k = 1.0f / (6.0f * st);
+  *fast = (k >= 0x1p-126f) && (k < 0x1p+127f);
+  return k;
 }
 
 // MXFP4: UE8M0 byte = clamp(floor(log2 absmax) - 2 + 127, 0, 254), read from
@@ -43,6 +74,17 @@ __device__ __forceinline__ float absmax8(const float (&v)[8]) {
   float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
   float b = fmaxf(fmaxf(fabsf(v[4]), fabsf(v[5])), fmaxf(fabsf(v[6]), fabsf(v[7])));
   return fmaxf(a, b);
+}
+
+__device__ __forceinline__ void unpack_bf16x8(const u32x4& w, float (&v)[8]) {
+  v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x); v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+  v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z); v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+}
+__device__ __forceinline__ void unpack_f32x8(const u32x4& a, const u32x4& b, float (&v)[8]) {
+  v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y);
+  v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+  v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y);
+  v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
 }
 
 // Codes of one octet under a decided block scale (software rounding; exact).
@@ -74,24 +116,50 @@ __device__ __forceinline__ uint32_t encode_octet_sw(const float (&v)[8], float s
 }
 
 // NVFP4 RTN codes of fl32(v / sdec) without a per-element division.
-// q0 = v * fl32(1/sdec) is within 2^-22 relative of fl32(v / sdec); RTN is
-// monotone in |q|, so when q0 * (1 - 2^-20) and q0 * (1 + 2^-20) round to
-// the same code, so does fl32(v / sdec).  Otherwise (an element within
-// ~2^-20 of a rounding threshold, about 1e-5 of them) the octet is redone
-// with IEEE divisions.  Blocks whose reciprocal is not a normal number go
-// straight to the division path.
+// With rc = v_rcp_f32(sdec) (1 ulp) and sdec in [2^-125, 2^125], the
+// products v * rc (1 - 2^-18) and v * rc (1 + 2^-18) bracket fl32(v / sdec)
+// in magnitude (all rounding errors together stay below 2^-21); RTN is
+// monotone in |q|, so when both round to the same code so does
+// fl32(v / sdec).  Otherwise (an element within ~2^-18 of a rounding
+// threshold) the octet is redone with IEEE divisions.
 __device__ __forceinline__ uint32_t encode_octet_nv_rtn(const float (&v)[8], float sdec, int64_t i) {
-  const float r = 1.0f / sdec;
-  if (r >= 0x1p-126f && r < 0x1p+127f) {          // a normal reciprocal: the 2^-22 bound holds
+  if (sdec >= 0x1p-125f && sdec <= 0x1p+125f) {
+    const float rc = __builtin_amdgcn_rcpf(sdec);
+    const float rlo = rc * 0x1.fffcp-1f;      // (1/sdec)(1 - 2^-18), within 2^-22
+    const float rhi = rc * 0x1.00004p+0f;     // (1/sdec)(1 + 2^-18), within 2^-22
     float lo[8], hi[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      float q0 = v[j] * r;
-      lo[j] = q0 * 0x1.fffffp-1f;        // 1 - 2^-20
-      hi[j] = q0 * 0x1.00001p+0f;        // 1 + 2^-20
+      lo[j] = v[j] * rlo;
+      hi[j] = v[j] * rhi;
     }
-    uint32_t wl = rtn8_unit(lo), wh = rtn8_unit(hi);
+    const uint32_t wl = rtn8_unit(lo), wh = rtn8_unit(hi);
     if (wl == wh) return wl;
+    // Some element sits within 2^-18 of a threshold.  Exact quotients are
+    // common there (short binary fractions over short scales), so refine
+    // each such element with one correction step and accept it when the
+    // remainder fma(-q1, sdec, v) is exactly zero, i.e. q1 * sdec == v and
+    // fl32(v / sdec) == q1.  With sdec in [2^-60, 2^60], |v| >= 2^-100 and
+    // |q1| near a threshold, a nonzero remainder is a multiple of 2^-123
+    // and cannot round to zero.
+    if (sdec >= 0x1p-60f && sdec <= 0x1p+60f) {
+      const uint32_t diff = wl ^ wh;
+      bool ok = true;
+      float qx[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        qx[j] = lo[j];
+        if ((diff >> (4 * j)) & 15u) {
+          const float q0 = v[j] * rc;
+          const float r0 = __builtin_fmaf(-q0, sdec, v[j]);
+          const float q1 = __builtin_fmaf(r0, rc, q0);
+          const float r1 = __builtin_fmaf(-q1, sdec, v[j]);
+          ok = ok && (r1 == 0.0f) && (fabsf(v[j]) >= 0x1p-100f);
+          qx[j] = q1;
+        }
+      }
+      if (ok) return rtn8_unit(qx);
+    }
   }
   return encode_octet_sw<false, false>(v, sdec, 0, i, 0, 0);
 }
@@ -117,22 +185,36 @@ __device__ __forceinline__ uint32_t encode_octet_mx_rtn(const u32x4& raw, const 
 }
 
 // ------------------------------------------------------------- quantize
-template <bool BF16, bool MX, bool SR>
+// Thread t of workgroup b owns octets b*256*U + t + 256*k, k < U: every
+// load and store instruction of a wave covers 64 consecutive octets, and
+// the U loads are issued before any of them is consumed.
+template <bool BF16, bool MX, bool SR, int U = kOctets<BF16>>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(
     const void* __restrict__ x, int64_t n_oct, const float* __restrict__ st_ptr, uint64_t seed,
     uint64_t step, uint32_t* __restrict__ packed, uint8_t* __restrict__ scales) {
   const float st = MX ? 1.0f : *st_ptr;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_oct; i += stride) {
-    float v[8];
-    u32x4 raw = {0u, 0u, 0u, 0u};
+  bool fast = false;
+  const float kinv = MX ? 0.0f : nv_kinv(st, &fast);
+  const int64_t base = (int64_t)blockIdx.x * (kThreads * U) + threadIdx.x;
+  u32x4 ra[U], rb[U];
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+    const int64_t i = base + (int64_t)k * kThreads;
+    const bool ok = i < n_oct;
     if constexpr (BF16) {
-      raw = ld_u32x4(static_cast<const uint8_t*>(x) + i * 16);
-      v[0] = bf16_lo(raw.x); v[1] = bf16_hi(raw.x); v[2] = bf16_lo(raw.y); v[3] = bf16_hi(raw.y);
-      v[4] = bf16_lo(raw.z); v[5] = bf16_hi(raw.z); v[6] = bf16_lo(raw.w); v[7] = bf16_hi(raw.w);
+      ra[k] = ok ? ld_u32x4(static_cast<const uint8_t*>(x) + i * 16) : u32x4{0u, 0u, 0u, 0u};
     } else {
-      load8<false>(x, i, v);
+      const uint8_t* p = static_cast<const uint8_t*>(x) + i * 32;
+      ra[k] = ok ? ld_u32x4(p) : u32x4{0u, 0u, 0u, 0u};
+      rb[k] = ok ? ld_u32x4(p + 16) : u32x4{0u, 0u, 0u, 0u};
     }
+  }
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+    const int64_t i = base + (int64_t)k * kThreads;
+    float v[8];
+    if constexpr (BF16) unpack_bf16x8(ra[k], v);
+    else unpack_f32x8(ra[k], rb[k], v);
     float am = absmax8(v);
     am = fmaxf(am, lane_xor1(am));
     if constexpr (MX) am = fmaxf(am, lane_xor2(am));
@@ -140,62 +222,74 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
     if constexpr (MX) {
       scode = mx_scale_byte(am);
       if constexpr (SR) word = encode_octet_sw<true, true>(v, 0.0f, 127 - (int)scode, i, seed, step);
-      else word = encode_octet_mx_rtn<BF16>(raw, v, scode);
+      else word = encode_octet_mx_rtn<BF16>(ra[k], v, scode);
     } else {
-      NvScale s = nv_block_scale(am, st);
+      const NvScale s = nv_block_scale(am, st, kinv, fast);
       scode = s.code;
       if constexpr (SR) word = encode_octet_sw<false, true>(v, s.sdec, 0, i, seed, step);
       else word = encode_octet_nv_rtn(v, s.sdec, i);
     }
-    st_u32(packed + i, word);
-    if ((i & (MX ? 3 : 1)) == 0) scales[i >> (MX ? 2 : 1)] = (uint8_t)scode;
+    if (i < n_oct) {
+      st_u32(packed + i, word);
+      if ((i & (MX ? 3 : 1)) == 0) scales[i >> (MX ? 2 : 1)] = (uint8_t)scode;
+    }
   }
 }
 
 // ----------------------------------------------------------- dequantize
-template <bool BF16OUT, bool MX>
+template <bool BF16OUT>
+__device__ __forceinline__ void mx_dequant_octet_hw(uint32_t w, uint32_t b, void* y, int64_t i) {
+  // scale 2^(b-127) is a normal float whose exponent field is b (1 <= b <= 254)
+  const float scale = __uint_as_float(b << 23);
+  if constexpr (BF16OUT) {
+    u32x4 o;
+    o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+    o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+    o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+    o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+    st_u32x4(static_cast<uint8_t*>(y) + i * 16, o);
+  } else {
+    float v[8];
+    e2m1x8_to_f32(w, scale, v);
+    store8<false>(y, i, v);
+  }
+}
+
+template <bool BF16OUT, bool MX, int U = 2>
 __global__ __launch_bounds__(kThreads) void dequantize_kernel(
     const uint32_t* __restrict__ packed, const uint8_t* __restrict__ scales,
     const float* __restrict__ st_ptr, int64_t n_oct, void* __restrict__ y) {
   const float st = MX ? 1.0f : *st_ptr;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_oct; i += stride) {
-    uint32_t w = packed[i];
-    uint32_t b = scales[i >> (MX ? 2 : 1)];
+  const int64_t base = (int64_t)blockIdx.x * (kThreads * U) + threadIdx.x;
+  uint32_t w[U], b[U];
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+    const int64_t i = base + (int64_t)k * kThreads;
+    const bool ok = i < n_oct;
+    w[k] = ok ? __builtin_nontemporal_load(packed + i) : 0u;
+    b[k] = ok ? scales[i >> (MX ? 2 : 1)] : 0u;
+  }
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+    const int64_t i = base + (int64_t)k * kThreads;
+    if (i >= n_oct) continue;
     float v[8];
     if constexpr (MX) {
-      if (b - 1u < 254u) {
-        // scale 2^(b-127) is a normal float whose exponent field is b
-        const float scale = __uint_as_float(b << 23);
-        if constexpr (BF16OUT) {
-          u32x4 o;
-          o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
-          o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
-          o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
-          o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
-          st_u32x4(static_cast<uint8_t*>(y) + i * 16, o);
-        } else {
-          typedef float f32x2 __attribute__((ext_vector_type(2)));
-          f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 0);
-          f32x2 bb = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 1);
-          f32x2 c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 2);
-          f32x2 d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 3);
-          v[0] = a.x; v[1] = a.y; v[2] = bb.x; v[3] = bb.y;
-          v[4] = c.x; v[5] = c.y; v[6] = d.x; v[7] = d.y;
-          store8<false>(y, i, v);
-        }
+      if (b[k] - 1u < 254u) {
+        mx_dequant_octet_hw<BF16OUT>(w[k], b[k], y, i);
         continue;
       }
-      int k = (int)b - 127;
+      // UE8M0 0 (2^-127) and 0xFF (NaN) in software
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        float e = e2m1_value((w >> (4 * j)) & 15u);
-        v[j] = (b == 255u) ? __builtin_nanf("") : __builtin_amdgcn_ldexpf(e, k);
+        const float e = e2m1_value((w[k] >> (4 * j)) & 15u);
+        v[j] = (b[k] == 255u) ? __builtin_nanf("") : __builtin_amdgcn_ldexpf(e, -127);
       }
     } else {
-      float sdec = e4m3_value_signed(b) * st;
+      const float sdec = e4m3_value_signed(b[k]) * st;
+      e2m1x8_to_f32(w[k], 1.0f, v);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = e2m1_value((w >> (4 * j)) & 15u) * sdec;
+      for (int j = 0; j < 8; ++j) v[j] = v[j] * sdec;
     }
     store8<BF16OUT>(y, i, v);
   }
@@ -204,28 +298,44 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(
 // --------------------------------------------------- tensor amax (NVFP4)
 __global__ void zero_u32_kernel(uint32_t* p) { *p = 0u; }
 
-// max |x (+ r)| over the tensor into *out_bits (atomic max on the bit pattern
-// of a non-negative float, which orders like the value).
+// max |x (+ r)| over the tensor into *out_bits: each workgroup reduces its
+// share (waves by DPP/shuffle, then LDS) and issues one atomic max on the
+// bit pattern of a non-negative float, which orders like the value.
 template <bool BF16, bool RES>
 __global__ __launch_bounds__(kThreads) void amax_kernel(const void* __restrict__ x,
                                                         const float* __restrict__ r, int64_t n_oct,
                                                         uint32_t* __restrict__ out_bits) {
+  constexpr int U = 2;
+  __shared__ float part[kThreads / 64];
   float m = 0.0f;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_oct; i += stride) {
-    float v[8];
-    load8<BF16>(x, i, v);
-    if constexpr (RES) {
-      float rr[8];
-      load8<false>(r, i, rr);
+  const int64_t stride = (int64_t)gridDim.x * kThreads * U;
+  for (int64_t base = (int64_t)blockIdx.x * kThreads * U + threadIdx.x; base < n_oct; base += stride) {
+    float v[U][8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = v[j] + rr[j];
+    for (int k = 0; k < U; ++k) {
+      const int64_t i = base + (int64_t)k * kThreads;
+      if (i < n_oct) load8<BF16>(x, i, v[k]);
+      else for (int j = 0; j < 8; ++j) v[k][j] = 0.0f;
+      if constexpr (RES) {
+        float rr[8];
+        if (i < n_oct) load8<false>(r, i, rr);
+        else for (int j = 0; j < 8; ++j) rr[j] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[k][j] = v[k][j] + rr[j];
+      }
     }
-    m = fmaxf(m, absmax8(v));
+#pragma unroll
+    for (int k = 0; k < U; ++k) m = fmaxf(m, absmax8(v[k]));
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  if ((threadIdx.x & 63) == 0) atomicMax(out_bits, __float_as_uint(m));
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float b = part[0];
+    for (int w = 1; w < kThreads / 64; ++w) b = fmaxf(b, part[w]);
+    atomicMax(out_bits, __float_as_uint(b));
+  }
 }
 
 // S_t = fl32(A / 2688), 1 when that is 0; written over the amax in place.
@@ -241,34 +351,57 @@ __global__ __launch_bounds__(kThreads) void ef_qdq_kernel(
     const void* x, float* __restrict__ res, void* y, int64_t n_oct,
     const float* __restrict__ st_ptr, uint64_t seed, uint64_t step, uint32_t* __restrict__ packed,
     uint8_t* __restrict__ scales) {
+  constexpr int U = 2;
   const float st = *st_ptr;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_oct; i += stride) {
-    float v[8];
-    load8<BF16IN>(x, i, v);
+  bool fast = false;
+  const float kinv = nv_kinv(st, &fast);
+  const int64_t base = (int64_t)blockIdx.x * (kThreads * U) + threadIdx.x;
+  float v[U][8];
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+    const int64_t i = base + (int64_t)k * kThreads;
+    const bool ok = i < n_oct;
+    if (ok) load8<BF16IN>(x, i, v[k]);
+    else for (int j = 0; j < 8; ++j) v[k][j] = 0.0f;
     if constexpr (RES) {
       float rr[8];
-      load8<false>(res, i, rr);
+      if (ok) load8<false>(res, i, rr);
+      else for (int j = 0; j < 8; ++j) rr[j] = 0.0f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = v[j] + rr[j];
+      for (int j = 0; j < 8; ++j) v[k][j] = v[k][j] + rr[j];
     }
-    float am = absmax8(v);
+  }
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+    const int64_t i = base + (int64_t)k * kThreads;
+    float am = absmax8(v[k]);
     am = fmaxf(am, lane_xor1(am));
-    NvScale s = nv_block_scale(am, st);
+    const NvScale s = nv_block_scale(am, st, kinv, fast);
     uint32_t word;
-    if constexpr (SR) word = encode_octet_sw<false, true>(v, s.sdec, 0, i, seed, step);
-    else word = encode_octet_nv_rtn(v, s.sdec, i);
+    if constexpr (SR) word = encode_octet_sw<false, true>(v[k], s.sdec, 0, i, seed, step);
+    else word = encode_octet_nv_rtn(v[k], s.sdec, i);
+    if (i >= n_oct) continue;
     float o[8];
+    e2m1x8_to_f32(word, 1.0f, o);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float yv = e2m1_value((word >> (4 * j)) & 15u) * s.sdec;
-      o[j] = BF16OUT ? __uint_as_float(f32_to_bf16_rne(yv) << 16) : yv;
+    for (int j = 0; j < 8; ++j) o[j] = o[j] * s.sdec;
+    if constexpr (BF16OUT) {
+      // round to bf16 once; the residual is taken against the rounded values
+      uint32_t pr[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        pr[j] = pack_bf16x2(o[2 * j], o[2 * j + 1]);
+        o[2 * j] = __uint_as_float(pr[j] << 16);
+        o[2 * j + 1] = __uint_as_float(pr[j] & 0xFFFF0000u);
+      }
+      st_u32x4(static_cast<uint8_t*>(y) + i * 16, u32x4{pr[0], pr[1], pr[2], pr[3]});
+    } else {
+      store8<false>(y, i, o);
     }
-    store8<BF16OUT>(y, i, o);
     if constexpr (RES) {
       float rn[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) rn[j] = v[j] - o[j];
+      for (int j = 0; j < 8; ++j) rn[j] = v[k][j] - o[j];
       store8<false>(res, i, rn);
     }
     if constexpr (CODES) {
@@ -282,14 +415,15 @@ __global__ __launch_bounds__(kThreads) void ef_qdq_kernel(
 int launch_tensor_scale(const void* x, bool bf16, const float* res, int64_t n_oct, float* ts,
                         hipStream_t st) {
   hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(1), 0, st, reinterpret_cast<uint32_t*>(ts));
-  unsigned g = grid_for(n_oct, 256 * 8);
+  int64_t g = blocks_for(n_oct, 2);
+  if (g > 1024) g = 1024;
   uint32_t* bits = reinterpret_cast<uint32_t*>(ts);
   if (bf16) {
-    if (res) hipLaunchKernelGGL((amax_kernel<true, true>), dim3(g), dim3(kThreads), 0, st, x, res, n_oct, bits);
-    else     hipLaunchKernelGGL((amax_kernel<true, false>), dim3(g), dim3(kThreads), 0, st, x, res, n_oct, bits);
+    if (res) hipLaunchKernelGGL((amax_kernel<true, true>), dim3((unsigned)g), dim3(kThreads), 0, st, x, res, n_oct, bits);
+    else     hipLaunchKernelGGL((amax_kernel<true, false>), dim3((unsigned)g), dim3(kThreads), 0, st, x, res, n_oct, bits);
   } else {
-    if (res) hipLaunchKernelGGL((amax_kernel<false, true>), dim3(g), dim3(kThreads), 0, st, x, res, n_oct, bits);
-    else     hipLaunchKernelGGL((amax_kernel<false, false>), dim3(g), dim3(kThreads), 0, st, x, res, n_oct, bits);
+    if (res) hipLaunchKernelGGL((amax_kernel<false, true>), dim3((unsigned)g), dim3(kThreads), 0, st, x, res, n_oct, bits);
+    else     hipLaunchKernelGGL((amax_kernel<false, false>), dim3((unsigned)g), dim3(kThreads), 0, st, x, res, n_oct, bits);
   }
   hipLaunchKernelGGL(tensor_scale_finalize_kernel, dim3(1), dim3(1), 0, st, ts);
   return launch_status();
@@ -298,12 +432,12 @@ int launch_tensor_scale(const void* x, bool bf16, const float* res, int64_t n_oc
 template <bool BF16, bool MX>
 void launch_quantize_t(bool sr, const void* x, int64_t n_oct, const float* ts, uint64_t seed,
                        uint64_t step, uint32_t* packed, uint8_t* scales, hipStream_t st) {
-  unsigned g = grid_for(n_oct);
+  const dim3 g((unsigned)blocks_for(n_oct, kOctets<BF16>));
   if (sr)
-    hipLaunchKernelGGL((quantize_kernel<BF16, MX, true>), dim3(g), dim3(kThreads), 0, st, x, n_oct,
+    hipLaunchKernelGGL((quantize_kernel<BF16, MX, true>), g, dim3(kThreads), 0, st, x, n_oct,
                        ts, seed, step, packed, scales);
   else
-    hipLaunchKernelGGL((quantize_kernel<BF16, MX, false>), dim3(g), dim3(kThreads), 0, st, x,
+    hipLaunchKernelGGL((quantize_kernel<BF16, MX, false>), g, dim3(kThreads), 0, st, x,
                        n_oct, ts, seed, step, packed, scales);
 }
 
@@ -311,9 +445,9 @@ template <bool BF16IN, bool BF16OUT>
 void launch_ef_t(bool res, bool sr, bool codes, const void* x, float* r, void* y, int64_t n_oct,
                  const float* ts, uint64_t seed, uint64_t step, uint32_t* packed, uint8_t* scales,
                  hipStream_t st) {
-  unsigned g = grid_for(n_oct);
+  const dim3 g((unsigned)blocks_for(n_oct, 2));
 #define FP4MI_EF(RES, SR, CODES)                                                                 \
-  hipLaunchKernelGGL((ef_qdq_kernel<BF16IN, BF16OUT, RES, SR, CODES>), dim3(g), dim3(kThreads), \
+  hipLaunchKernelGGL((ef_qdq_kernel<BF16IN, BF16OUT, RES, SR, CODES>), g, dim3(kThreads),      \
                      0, st, x, r, y, n_oct, ts, seed, step, packed, scales)
   if (res) {
     if (sr) { if (codes) FP4MI_EF(true, true, true); else FP4MI_EF(true, true, false); }
@@ -324,6 +458,9 @@ void launch_ef_t(bool res, bool sr, bool codes, const void* x, float* r, void* y
   }
 #undef FP4MI_EF
 }
+
+// Exact grids must fit the x dimension of a launch.
+inline bool grid_fits(int64_t n_oct) { return blocks_for(n_oct, 1) <= 0x7FFFFFFF; }
 
 }  // namespace
 }  // namespace fp4mi
@@ -356,6 +493,7 @@ extern "C" int fp4_quantize(const void* x, int dtype, int64_t rows, int64_t cols
   hipStream_t st = as_stream(stream);
   const bool bf16 = dtype == FP4_DTYPE_BF16, sr = rounding == FP4_ROUND_SR;
   const int64_t n_oct = n / 8;
+  if (!grid_fits(n_oct)) return FP4_ESHAPE;
   if (!mx && tscale_mode == FP4_TSCALE_COMPUTE) {
     int rc = launch_tensor_scale(x, bf16, nullptr, n_oct, tensor_scale, st);
     if (rc) return rc;
@@ -392,7 +530,8 @@ extern "C" int fp4_dequantize(const uint8_t* packed, const uint8_t* scales,
     return FP4_EOVERLAP;
   hipStream_t st = as_stream(stream);
   const int64_t n_oct = n / 8;
-  unsigned g = grid_for(n_oct);
+  if (!grid_fits(n_oct)) return FP4_ESHAPE;
+  const dim3 g((unsigned)blocks_for(n_oct, 2));
   const uint32_t* pk = reinterpret_cast<const uint32_t*>(packed);
   if (out_dtype == FP4_DTYPE_BF16) {
     if (mx) hipLaunchKernelGGL((dequantize_kernel<true, true>), dim3(g), dim3(kThreads), 0, st, pk, scales, tensor_scale, n_oct, y);
@@ -439,6 +578,7 @@ extern "C" int fp4_errfeedback_qdq(const void* x, int dtype, int64_t rows, int64
   const bool bf16 = dtype == FP4_DTYPE_BF16, obf16 = out_dtype == FP4_DTYPE_BF16;
   const bool sr = rounding == FP4_ROUND_SR, codes = packed != nullptr;
   const int64_t n_oct = n / 8;
+  if (!grid_fits(n_oct)) return FP4_ESHAPE;
   if (tscale_mode == FP4_TSCALE_COMPUTE) {
     int rc = launch_tensor_scale(x, bf16, residual, n_oct, tensor_scale, st);
     if (rc) return rc;
