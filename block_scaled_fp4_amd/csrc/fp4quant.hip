@@ -185,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void fp4quant_decode_kernel(
     const int64_t t = base + (int64_t)k * kThreads;
     const bool ok = t < n_lane;
 #pragma unroll
-    for (int o = 0; o < OCT; ++o) w[k][o] = ok ? __builtin_nontemporal_load(packed + t * OCT + o) : 0u;
+    for (int o = 0; o < OCT; ++o) w[k][o] = ok ? packed[t * OCT + o] : 0u;
     f[k] = ok ? (s_rms[t / LPG] * s_abs[t / LPG]) * c_dec : 0.0f;
   }
 #pragma unroll

@@ -4,39 +4,52 @@
 // 4-to-1 scale alignment, item 2 the fused FP4RowToFP8Col kernel, item 3
 // precomputed ragged shard offsets).
 //
-// Tiling.  A workgroup owns 64 consecutive tokens of the concatenated token
-// axis, which may hold pieces ("segments") of several experts, and a run of
-// 128-channel FP8 blocks.  Per FP8 block it
-//   1. loads the 64 x 64 code bytes (a thread holds one 32-code MXFP4
-//      sub-block of one token; a wave reads 16 tokens x 64 contiguous bytes)
-//      and each token's four UE8M0 bytes as one dword;
-//   2. takes S_tgt = max of the four bytes, d = S_tgt - S_sub, and remaps the
-//      codes to E4M3 bytes through an 8-entry byte table per shift d
-//      (v_perm_b32 does 4 lookups at once); the tables come from the
-//      exponent-field mapping E8 = E4 - 1 + 7 - d, built once per workgroup;
-//   3. transposes 4 x 4 byte blocks across the 4 lanes that hold 4
-//      consecutive tokens (two DPP quad permutes + v_perm_b32), giving
-//      dwords of 4 tokens of one channel;
-//   4. stages them in LDS as [channel][token] rows of 16 dwords plus one pad
-//      dword, the token-dword index XOR-swizzled by the sub-block so the
-//      writes of a wave spread over the banks;
-//   5. writes every output row with aligned dword stores: each output dword
-//      is cut out of two LDS dwords with v_alignbyte_b32, so the per-row
-//      misalignment of the ragged [H, n_e] matrices costs nothing; only the
-//      partial dwords at segment edges fall back to byte stores;
-//   6. writes the fp32 block scales 2^(S_tgt - 127).
-// Segment bounds are checked against [0, T] per expert, so a malformed
-// offsets array cannot cause out-of-bounds writes.
+// Work decomposition.  The token space is cut into chunks of kChunk tokens;
+// workgroup (chunk, b) converts FP8 block b (128 channels) of every expert
+// piece in its chunk, and its four waves take the four 32-channel MXFP4
+// sub-blocks.  Piece boundaries are snapped to multiples of 4 tokens of the
+// expert, so neighbouring chunks agree on them.  A wave streams through its
+// piece 252 new tokens at a time (lane L >= 1 holds 4 consecutive tokens;
+// lane 0 re-reads the 4 before them) and writes its 32 output rows, which lie
+// one after the other in memory, as a stream of aligned dwords:
+//   1. per token: load the 16 code bytes and the four UE8M0 bytes (one
+//      dword), S_tgt = max of the four, d = S_tgt - S_sub, remap the codes to
+//      E4M3 bytes through an 8-entry byte table per shift d (v_perm_b32 does
+//      4 lookups at once); the tables come from the exponent-field mapping
+//      E8 = E4 - 1 + 7 - d, built once per workgroup;
+//   2. transpose 4 x 4 byte blocks inside the lane (v_perm_b32), giving per
+//      channel a dword of the lane's 4 tokens;
+//   3. a row starting m = (address mod 4) bytes past a dword boundary is
+//      written with aligned dwords cut (v_alignbyte_b32) from the lane's
+//      dword and the one of the lane before it (a DPP wavefront shift); the
+//      dword shared by the end of row h and the start of row h+1 is stitched
+//      with row h+1's first 4 tokens by the piece that ends the expert.
+// Loads go through buffer resources whose range check returns zero for
+// tokens outside the piece, so no load sits in a branch, and the next tile's
+// loads are issued before the current tile's stores.  Chunks are laid out so
+// that neighbouring chunks (which share output lines at their seams) and the
+// two blocks that share input lines run in one L2 domain.  Only experts of
+// fewer than 4 tokens need byte stores.  Expert ranges are clamped to
+// [0, T], so a malformed offsets array cannot cause out-of-bounds accesses.
 #include "device_common.hpp"
 #include "host_common.hpp"
 
 namespace fp4mi {
 namespace {
 
-constexpr int kTok = 64;         // tokens per tile
-constexpr int kRowDw = 17;       // LDS dwords per channel row: 16 token dwords + 1 pad
 constexpr int kMaxShift = 15;    // shifts >= 13 already map every value to 0
-constexpr int kMaxSeg = 64;      // a 64-token tile holds at most 64 non-empty segments
+// Buffer resource word 3 for raw (untyped, stride 0) buffer access on gfx9.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kTileNew = 252;    // new tokens per wave step (4 per lane, lanes 1..63)
+constexpr int kChunk = 4 * kTileNew;   // positions of the padded token space per workgroup
+// Each expert is followed by kPad positions of padding in the space that is
+// cut into chunks: a piece costs about a tile of work beyond its tokens, so
+// no chunk holds more than a few pieces.
+constexpr int kPad = kTileNew;
+constexpr int kXcds = 8;               // L2 domains the workgroups are spread over
+// A load offset past every load window (windows stay below 2^30 bytes for
+// H < 2^21): a token loaded at it reads as zero.
+constexpr int kOutside = 0x7FFFFFF0;
 
 // E4M3 magnitude byte of e2m1 magnitude m3 scaled by 2^-d, by exponent-field
 // remapping.  Write the E2M1 magnitude as (2 + M) * 2^(E - 2) with E its
@@ -67,184 +80,237 @@ __device__ __forceinline__ uint32_t lookup4(uint32_t nib, uint32_t tab_lo, uint3
   return __builtin_amdgcn_perm(tab_hi, tab_lo, mag) | sgn;
 }
 
-__device__ __forceinline__ uint32_t dpp_xor1_u(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
-}
-__device__ __forceinline__ uint32_t dpp_xor2_u(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
-}
-
-// Physical LDS dword of logical token-dword c (0..16) in channel row h.
-__device__ __forceinline__ int lds_col(int h, int c) {
-  return (c < 16) ? (c ^ (((h >> 5) & 3) << 2)) : c;
-}
-
-struct Segment {
-  int64_t e_off;   // first token of the expert
-  int64_t n;       // tokens of the expert
-  int a, b;        // tile-local token range [a, b) of this segment
+struct TileIn {
+  u32x4 w[4];        // code bytes of the lane's 4 tokens (one 32-channel sub-block)
+  uint32_t s[4];     // their four UE8M0 block scales
 };
 
-__global__ __launch_bounds__(kThreads) void fp8col_kernel(
-    const uint8_t* __restrict__ packed, const uint8_t* __restrict__ sb,
-    const int64_t* __restrict__ off, int E, int64_t T, int64_t H, int blocks_per_wg,
-    uint8_t* __restrict__ out, float* __restrict__ sc_out) {
-  __shared__ uint32_t tile[128 * kRowDw];
-  __shared__ uint32_t lut[(kMaxShift + 1) * 2];
-  __shared__ Segment seg[kMaxSeg];
-  __shared__ int32_t tgt[kTok];
-  __shared__ int s_nseg;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int64_t t0 = (int64_t)blockIdx.x * kTok;
-  const int64_t t_end = (t0 + kTok < T) ? t0 + kTok : T;
-  const int64_t HB = H / 128;
-
-  // byte tables, one 8-byte table per shift d (bytes indexed by m3)
-  if (tid < (kMaxShift + 1) * 2) {
-    const int d = tid >> 1, half = tid & 1;
-    uint32_t w = 0;
-    for (int b = 0; b < 4; ++b) w |= remap_e2m1_to_e4m3((uint32_t)(4 * half + b), d) << (8 * b);
-    lut[tid] = w;
+// Loads the 4 tokens starting `first` tokens into the load window.
+__device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs,
+                                          int first, bool valid0, int cstride, int sstride,
+                                          TileIn& x) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const bool ok = valid0 || (first + j >= 4);
+    const int tok = first + j;
+    x.w[j] = __builtin_amdgcn_raw_buffer_load_b128(rc, ok ? tok * cstride : kOutside, 0, 0);
+    x.s[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, ok ? tok * sstride : kOutside, 0, 0);
   }
+}
 
-  // ---- segments of this tile (wave 0)
-  if (tid < 64) {
-    // expert of the first token: largest e < E with off[e] <= t0 (64-way search)
-    int64_t lo = 0, hi = E;
-    while (hi - lo > 1) {
-      const int64_t step = (hi - lo + 63) / 64;
-      const int64_t idx = lo + (int64_t)lane * step;
-      const bool ok = idx < hi && off[idx] <= t0;
-      const uint64_t m = __ballot(ok);
-      const int top = 63 - __builtin_clzll(m | 1ull);
-      lo = lo + (int64_t)top * step;
-      hi = (lo + step < hi) ? lo + step : hi;
-    }
-    int nseg = 0;
-    for (int64_t e0 = lo; e0 < E && nseg < kMaxSeg; e0 += 64) {
-      const int64_t e = e0 + lane;
-      const int64_t a_e = (e < E) ? off[e] : T;
-      int64_t b_e = (e < E) ? off[e + 1] : T;
-      if (b_e > T) b_e = T;
-      const int64_t s0 = (a_e > t0) ? a_e : t0;
-      const int64_t s1 = (b_e < t_end) ? b_e : t_end;
-      const bool keep = e < E && a_e >= 0 && s0 < s1;
-      const uint64_t m = __ballot(keep);
-      const int pos = nseg + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-      if (keep && pos < kMaxSeg) {
-        Segment sg;
-        sg.e_off = a_e;
-        sg.n = b_e - a_e;
-        sg.a = (int)(s0 - t0);
-        sg.b = (int)(s1 - t0);
-        seg[pos] = sg;
-      }
-      nseg += __builtin_popcountll(m);
-      // stop once this window reaches the end of the tile
-      const int64_t last_b = __shfl(b_e, 63);
-      if (last_b >= t_end || e0 + 64 >= E) break;
-    }
-    if (lane == 0) s_nseg = nseg < kMaxSeg ? nseg : kMaxSeg;
-  }
-
-  // load-phase roles: token t = 4*(tid>>4) + (tid&3), sub-block (tid>>2)&3
-  const int r = tid & 3, sub = (tid >> 2) & 3;
-  const int tl = 4 * (tid >> 4) + r;
-  const int64_t gl = t0 + tl;
-  const bool lvalid = gl < T;
-  const uint32_t sel1 = (r & 1) ? 0x03070105u : 0x06020400u;
-  const uint32_t sel2 = (r & 2) ? 0x03020706u : 0x05040100u;
-  const uint8_t* src_codes = packed + (lvalid ? gl : 0) * (H / 2) + sub * 16;
-  const uint8_t* src_scales = sb + (lvalid ? gl : 0) * (H / 32);
-  // this thread's LDS destinations: rows 32 sub + 4 g + r, swizzled token dword
-  uint32_t* dst0 = tile + (32 * sub + r) * kRowDw + ((tid >> 4) ^ (sub << 2));
-  // store-phase roles: 16 lanes per channel row, 16 rows per pass
-  const int q = tid & 15, hr = tid >> 4;
-
-  const int64_t b_begin = (int64_t)blockIdx.y * blocks_per_wg;
-  const int64_t b_end = (b_begin + blocks_per_wg < HB) ? b_begin + blocks_per_wg : HB;
-
-  // software pipeline: the codes and scales of block b are in registers
-  // while block b-1 is being written out
-  u32x4 w = {0u, 0u, 0u, 0u};
-  uint32_t s4 = 0;
-  if (lvalid && b_begin < b_end) {
-    w = ld_u32x4(src_codes + b_begin * 64);
-    s4 = *reinterpret_cast<const uint32_t*>(src_scales + b_begin * 4);
-  }
-  __syncthreads();            // LUT and segments ready (see above)
-  const int nseg = s_nseg;
-
-  for (int64_t b = b_begin; b < b_end; ++b) {
-    // ---- 1-2: scale alignment and remap of block b
+// Remaps the lane's 4 tokens of sub-block `sub` to E4M3 and transposes them:
+// Y[c] holds channel c of the 4 tokens, token j in byte j.  tgt[j] is S_tgt.
+__device__ __forceinline__ void convert_tile(const TileIn& x, int sub, const uint32_t* lut,
+                                             uint32_t Y[32], uint32_t tgt[4]) {
+  uint32_t X[4][8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t s4 = x.s[j];
     const uint32_t s_tgt = max(max(s4 & 0xFFu, (s4 >> 8) & 0xFFu),
                                max((s4 >> 16) & 0xFFu, s4 >> 24));
     const uint32_t s_sub = (s4 >> (8 * sub)) & 0xFFu;
     const int d = min((int)(s_tgt - s_sub), kMaxShift);
     const uint32_t tlo = lut[2 * d], thi = lut[2 * d + 1];
-    uint32_t D[8];
-    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+    const uint32_t ww[4] = {x.w[j].x, x.w[j].y, x.w[j].z, x.w[j].w};
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t ev = lookup4(ww[k], tlo, thi);          // channels 8k+0,2,4,6
-      const uint32_t od = lookup4(ww[k] >> 4, tlo, thi);     // channels 8k+1,3,5,7
-      D[2 * k] = __builtin_amdgcn_perm(od, ev, 0x05010400u);
-      D[2 * k + 1] = __builtin_amdgcn_perm(od, ev, 0x07030602u);
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t ev = lookup4(ww[q], tlo, thi);         // channels 8q+0,2,4,6
+      const uint32_t od = lookup4(ww[q] >> 4, tlo, thi);    // channels 8q+1,3,5,7
+      X[j][2 * q] = __builtin_amdgcn_perm(od, ev, 0x05010400u);
+      X[j][2 * q + 1] = __builtin_amdgcn_perm(od, ev, 0x07030602u);
     }
-    // ---- 3-4: 4x4 byte transpose across the token quad, stage in LDS
+    tgt[j] = s_tgt;
+  }
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      const uint32_t t1 = __builtin_amdgcn_perm(dpp_xor1_u(D[g]), D[g], sel1);
-      const uint32_t t2 = __builtin_amdgcn_perm(dpp_xor2_u(t1), t1, sel2);
-      dst0[4 * g * kRowDw] = t2;
-    }
-    if (sub == 0) tgt[tl] = (int32_t)s_tgt;
-    __syncthreads();
-    // prefetch block b+1 while block b is written out
-    if (lvalid && b + 1 < b_end) {
-      w = ld_u32x4(src_codes + (b + 1) * 64);
-      s4 = *reinterpret_cast<const uint32_t*>(src_scales + (b + 1) * 4);
-    }
-    // ---- 5-6: aligned dword stores per segment and channel row
-    for (int si = 0; si < nseg; ++si) {
-      const Segment sg = seg[si];
-      const int a = sg.a, bb = sg.b;
-      // byte address of tile token 0 in channel row 128 b + hr of this expert
-      int64_t rt = H * sg.e_off + (t0 - sg.e_off) + (128 * b + hr) * sg.n;
-      const int64_t rstep = 16 * sg.n;
-#pragma unroll
-      for (int p = 0; p < 8; ++p, rt += rstep) {
-        const int h = 16 * p + hr;
-        const uint32_t* row = tile + h * kRowDw;
-        const int colx = ((p >> 1) & 3) << 2;                 // swizzle of rows 32s..32s+31
-        const int m = (int)(((uint32_t)rt + (uint32_t)a) & 3u);
-        const int am = a - m;                                 // tile token of the first dword's byte 0
-        const int base_c = am >> 2, sh = am & 3;              // floor / remainder (am >= -3)
-        for (int item = q; item < 17; item += 16) {
-          const int tt0 = am + 4 * item;
-          if (tt0 >= bb) break;
-          const int c = base_c + item;
-          const int c0 = max(c, 0), c1 = c + 1;
-          const uint32_t lo_dw = row[c0 < 16 ? (c0 ^ colx) : 16];
-          const uint32_t hi_dw = row[c1 < 16 ? (c1 ^ colx) : 16];
-          const uint32_t val = __builtin_amdgcn_alignbyte(hi_dw, lo_dw, (uint32_t)sh);
-          const int blo = max(a - tt0, 0), bhi = min(bb - tt0, 4);
-          uint8_t* A = out + rt + tt0;
-          if (blo == 0 && bhi == 4) {
-            *reinterpret_cast<uint32_t*>(A) = val;
-          } else {
-            for (int k = blo; k < bhi; ++k) A[k] = (uint8_t)(val >> (8 * k));
-          }
-        }
+  for (int g = 0; g < 8; ++g) {
+    const uint32_t a0 = X[0][g], a1 = X[1][g], a2 = X[2][g], a3 = X[3][g];
+    const uint32_t l01 = __builtin_amdgcn_perm(a1, a0, 0x05010400u);   // a0.b0 a1.b0 a0.b1 a1.b1
+    const uint32_t h01 = __builtin_amdgcn_perm(a1, a0, 0x07030602u);   // a0.b2 a1.b2 a0.b3 a1.b3
+    const uint32_t l23 = __builtin_amdgcn_perm(a3, a2, 0x05010400u);
+    const uint32_t h23 = __builtin_amdgcn_perm(a3, a2, 0x07030602u);
+    Y[4 * g + 0] = __builtin_amdgcn_perm(l23, l01, 0x05040100u);
+    Y[4 * g + 1] = __builtin_amdgcn_perm(l23, l01, 0x07060302u);
+    Y[4 * g + 2] = __builtin_amdgcn_perm(h23, h01, 0x05040100u);
+    Y[4 * g + 3] = __builtin_amdgcn_perm(h23, h01, 0x07060302u);
+  }
+}
+
+__device__ __forceinline__ int64_t round_up4(int64_t v) { return (v + 3) & ~int64_t(3); }
+__device__ __forceinline__ int64_t clamp64(int64_t v, int64_t lo, int64_t hi) {
+  return v < lo ? lo : (v > hi ? hi : v);
+}
+
+__global__ __launch_bounds__(kThreads) void fp8col_kernel(
+    const uint8_t* __restrict__ packed, const uint8_t* __restrict__ sb,
+    const int64_t* __restrict__ off, int32_t E, int64_t T, int64_t H, int64_t nchunks,
+    int64_t per_xcd, uint8_t* __restrict__ out, float* __restrict__ sc_out) {
+  __shared__ uint32_t lut[(kMaxShift + 1) * 2];
+  __shared__ int counts[2];
+  const int tid = threadIdx.x;
+  // the wave index is uniform across a wave; saying so keeps the buffer
+  // resources built from it in scalar registers
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // Workgroup -> (chunk, block).  Consecutive workgroups go to the L2 domains
+  // in turn; domain x takes chunks [x per_xcd, (x + 1) per_xcd), block fastest.
+  const int64_t HB = H / 128;
+  const int64_t id = blockIdx.x;
+  const int64_t slot = id / kXcds;
+  const int64_t chunk = (id % kXcds) * per_xcd + slot / HB;
+  const int64_t b = slot % HB;
+  if (chunk >= nchunks) return;                         // uniform per workgroup
+  const int64_t g0 = chunk * kChunk, g1 = g0 + kChunk;
+
+  if (tid < (kMaxShift + 1) * 2) {
+    const int d = tid >> 1, half = tid & 1;
+    uint32_t w = 0;
+    for (int k = 0; k < 4; ++k) w |= remap_e2m1_to_e4m3((uint32_t)(4 * half + k), d) << (8 * k);
+    lut[tid] = w;
+  }
+  if (tid < 2) counts[tid] = 0;
+  __syncthreads();
+  // Expert e starts at position off[e] + kPad e of the padded space.
+  // Experts with a piece in this chunk: from the last one starting at or
+  // before g0 up to the last one starting before g1 (offsets ascend).
+  int c0 = 0, c1 = 0;
+  for (int e = tid; e < E; e += kThreads) {
+    const int64_t o = off[e] + (int64_t)kPad * e;
+    c0 += o <= g0;
+    c1 += o < g1;
+  }
+  if (c0) atomicAdd(&counts[0], c0);
+  if (c1) atomicAdd(&counts[1], c1);
+  __syncthreads();
+  const int e_first = max(counts[0] - 1, 0), e_end = counts[1];
+
+  const int h0 = 32 * wave;                             // first channel of the wave's run
+  const int cs = (int)(H / 2), ss = (int)(H / 32);      // token strides of codes and scales
+  for (int e = e_first; e < e_end; ++e) {               // uniform per workgroup
+    const int64_t off_e = clamp64(off[e], 0, T);
+    const int64_t end_e = clamp64(off[e + 1], off_e, T);
+    const int n = (int)(end_e - off_e);                 // n < 2^26 (checked by the host)
+    const int64_t pos = off_e + (int64_t)kPad * e;     // the expert's padded position
+    const int a = (int)clamp64(round_up4(g0 - pos), 0, n);
+    const int bb = (int)clamp64(round_up4(g1 - pos), 0, n);
+    if (a >= bb) continue;
+    const bool last = bb == n;
+    const int len = bb - a;
+    const int ntiles = (len + (last ? 3 : 0) + kTileNew - 1) / kTileNew;
+    const int64_t R0 = H * off_e + (128 * b + h0) * (int64_t)n;   // the run of 32 rows
+    float* const so = sc_out + HB * off_e + b * n;
+
+    if (n < 4) {
+      // Experts of 1..3 tokens: one piece; rows shorter than a dword, so each
+      // output byte is computed and stored on its own.
+      for (int i = lane; i < 32 * n; i += 64) {
+        const int r = i / n, t = i - r * n;
+        const int ch = 32 * wave + r;                   // channel within the block
+        const int64_t tok = off_e + t;
+        const uint32_t s4 = *reinterpret_cast<const uint32_t*>(sb + tok * ss + 4 * b);
+        const uint32_t s_tgt = max(max(s4 & 0xFFu, (s4 >> 8) & 0xFFu),
+                                   max((s4 >> 16) & 0xFFu, s4 >> 24));
+        const uint32_t s_sub = (s4 >> (8 * wave)) & 0xFFu;
+        const int d = min((int)(s_tgt - s_sub), kMaxShift);
+        const uint32_t code = (packed[tok * cs + 64 * b + ch / 2] >> (4 * (ch & 1))) & 0xFu;
+        const uint32_t v = lookup4(code, lut[2 * d], lut[2 * d + 1]) & 0xFFu;
+        out[R0 + (int64_t)r * n + t] = (uint8_t)v;
+        if (wave == 0 && r == 0) so[t] = __builtin_amdgcn_ldexpf(1.0f, (int)s_tgt - 127);
       }
-      if (tid >= a && tid < bb)
-        sc_out[HB * sg.e_off + b * sg.n + (t0 + tid - sg.e_off)] =
-            __builtin_amdgcn_ldexpf(1.0f, tgt[tid] - 127);
+      continue;
     }
-    __syncthreads();
+
+    // Stores go through the run's window, which begins 8 bytes before the run
+    // (R0 is a multiple of 32, so every dword offset is positive) and ends
+    // with it; the buffer range check drops stores at kOutside.
+    const __amdgpu_buffer_rsrc_t win = __builtin_amdgcn_make_buffer_rsrc(
+        out + R0 - 8, (short)0, 32 * n + 8, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t wsc = __builtin_amdgcn_make_buffer_rsrc(
+        so, (short)0, 4 * n, kBufferWord3);
+    // Load windows: tokens a - 4 .. bb - 1 of the expert.
+    const int64_t wtok = off_e + a - 4;
+    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(packed) + wtok * cs + 64 * b + 16 * wave, (short)0, (len + 4) * cs,
+        kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(sb) + wtok * ss + 4 * b, (short)0, (len + 4) * ss, kBufferWord3);
+    const bool valid0 = a > 0;                          // the 4 tokens before the piece exist
+
+    // Row heads (tokens 0..3 of row c in lane c) for the stitched row ends of
+    // a piece that ends the expert: from tile 0 when the piece also starts
+    // it, else loaded here.
+    uint32_t hv = 0;
+    if (last && a > 0) {
+      TileIn hx;
+      const uint8_t* c0p = packed + off_e * cs + 64 * b + 16 * wave;
+      const uint8_t* s0p = sb + off_e * ss + 4 * b;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        hx.w[j] = *reinterpret_cast<const u32x4*>(c0p + j * cs);
+        hx.s[j] = *reinterpret_cast<const uint32_t*>(s0p + j * ss);
+      }
+      uint32_t Yh[32], th[4];
+      convert_tile(hx, wave, lut, Yh, th);
+#pragma unroll
+      for (int c = 0; c < 32; ++c) hv = lane == c ? Yh[c] : hv;
+    }
+
+    // Tiles alternate between two load buffers.  Every tile issues the same
+    // memory operations (the next tile's 8 loads, then 33 stores), so the
+    // loads of tile k + 1 stay in flight while tile k is converted and
+    // stored, and the wait for them leaves tile k's stores outstanding.
+    auto process = [&](const TileIn& x, int k) {
+      uint32_t Y[32], tgt[4];
+      convert_tile(x, wave, lut, Y, tgt);
+      const int tl = a - 4 + kTileNew * k + 4 * lane;   // the lane's first token
+      if (last && a == 0 && k == 0) {
+#pragma unroll
+        for (int c = 0; c < 32; ++c)                    // lane 1 holds tokens 0..3
+          hv = lane == c ? (uint32_t)__builtin_amdgcn_readlane(Y[c], 1) : hv;
+      }
+
+      // wave w stores the FP8 block scale of the lane's token w
+      const uint32_t tg = wave == 0 ? tgt[0] : wave == 1 ? tgt[1] : wave == 2 ? tgt[2] : tgt[3];
+      const bool sc_ok = lane > 0 && tl + wave < bb;
+      __builtin_amdgcn_raw_buffer_store_b32(
+          __float_as_uint(__builtin_amdgcn_ldexpf(1.0f, (int)tg - 127)), wsc,
+          sc_ok ? 4 * (tl + wave) : kOutside, 0, 0);
+
+      // Aligned dword stores along each row.  Lane L >= 1 writes the dword
+      // starting at row token tf = tl - m; the piece owns tf in [0, bb - m),
+      // or [0, n) when it ends the expert (tf < 0 is a row head, written
+      // with the end of the row before).  A row end dword (tf + 4 > n) takes
+      // the next row's first tokens; a run ends dword aligned, so row 31
+      // never has one.
+#pragma unroll
+      for (int c = 0; c < 32; ++c) {
+        const int rowoff = c * n;                       // row c starts at run byte c n
+        const int m = rowoff & 3;
+        const uint32_t own = Y[c];
+        // lane L - 1's dword (wavefront shift right by one lane)
+        const uint32_t prev =
+            (uint32_t)__builtin_amdgcn_update_dpp(0, (int)own, 0x138, 0xf, 0xf, false);
+        const int tf = tl - m;
+        uint32_t val = (m == 0) ? own : __builtin_amdgcn_alignbyte(own, prev, (uint32_t)(4 - m));
+        const bool owned = lane > 0 && tf >= 0 && tf < (last ? n : bb - m);
+        if (c < 31 && tf + 4 > n && owned) {
+          const int hi = n - tf;                        // 1..3 bytes of this row
+          const uint32_t mask = (1u << (8 * hi)) - 1u;
+          val = (val & mask) | ((uint32_t)__builtin_amdgcn_readlane(hv, c + 1) << (8 * hi));
+        }
+        __builtin_amdgcn_raw_buffer_store_b32(val, win, owned ? 8 + rowoff + tf : kOutside, 0, 0);
+      }
+    };
+    TileIn A, B;
+    load_tile(rc, rs, 4 * lane, valid0, cs, ss, A);
+    __builtin_amdgcn_s_waitcnt(0);                      // A is in: every entry to the loop alike
+    for (int k = 0;; k += 2) {
+      load_tile(rc, rs, kTileNew * (k + 1) + 4 * lane, valid0, cs, ss, B);
+      process(A, k);
+      if (k + 1 >= ntiles) break;
+      load_tile(rc, rs, kTileNew * (k + 2) + 4 * lane, valid0, cs, ss, A);
+      process(B, k + 1);
+      if (k + 2 >= ntiles) break;
+    }
   }
 }
 
@@ -259,6 +325,8 @@ extern "C" int mxfp4_row_to_fp8_col(const uint8_t* packed, const uint8_t* scales
                                     float* fp8_scales, void* stream) {
   if (num_experts < 1) return FP4_EINVAL;
   if (total_tokens < 0 || hidden <= 0 || hidden % 128) return FP4_ESHAPE;
+  // 32-bit offsets in the load and store windows
+  if (total_tokens >= (int64_t(1) << 26) || hidden >= (int64_t(1) << 21)) return FP4_ESHAPE;
   int64_t n;
   if (!checked_count(total_tokens, hidden, &n)) return FP4_ESHAPE;
   if (!token_offsets) return FP4_EINVAL;
@@ -276,13 +344,13 @@ extern "C" int mxfp4_row_to_fp8_col(const uint8_t* packed, const uint8_t* scales
       return FP4_EOVERLAP;
   if (overlaps(fp8_out, ob, fp8_scales, scb)) return FP4_EOVERLAP;
   hipStream_t st = as_stream(stream);
-  const int64_t tiles = (total_tokens + kTok - 1) / kTok;
   const int64_t HB = hidden / 128;
-  const int bpw = (int)(HB < 8 ? HB : 8);
-  const int64_t gy = (HB + bpw - 1) / bpw;
-  if (tiles > 0x7FFFFFFF || gy > 65535) return FP4_ESHAPE;
-  hipLaunchKernelGGL(fp8col_kernel, dim3((unsigned)tiles, (unsigned)gy), dim3(kThreads), 0, st,
-                     packed, scales_e8m0, token_offsets, (int)num_experts, total_tokens, hidden,
-                     bpw, fp8_out, fp8_scales);
+  const int64_t nchunks = (total_tokens + (int64_t)kPad * num_experts + kChunk - 1) / kChunk;
+  const int64_t per_xcd = (nchunks + kXcds - 1) / kXcds;
+  const int64_t grid = kXcds * per_xcd * HB;
+  if (grid > 0x7FFFFFFF) return FP4_ESHAPE;
+  hipLaunchKernelGGL(fp8col_kernel, dim3((unsigned)grid), dim3(kThreads), 0, st, packed,
+                     scales_e8m0, token_offsets, num_experts, total_tokens, hidden, nchunks,
+                     per_xcd, fp8_out, fp8_scales);
   return launch_status();
 }

@@ -143,20 +143,21 @@ __device__ __forceinline__ uint32_t encode_octet_nv_rtn(const float (&v)[8], flo
     // |q1| near a threshold, a nonzero remainder is a multiple of 2^-123
     // and cannot round to zero.
     if (sdec >= 0x1p-60f && sdec <= 0x1p+60f) {
+      // branch-free over the octet: elements whose bracket agreed keep that
+      // code (through lo); the others must be certified exact
       const uint32_t diff = wl ^ wh;
       bool ok = true;
       float qx[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        qx[j] = lo[j];
-        if ((diff >> (4 * j)) & 15u) {
-          const float q0 = v[j] * rc;
-          const float r0 = __builtin_fmaf(-q0, sdec, v[j]);
-          const float q1 = __builtin_fmaf(r0, rc, q0);
-          const float r1 = __builtin_fmaf(-q1, sdec, v[j]);
-          ok = ok && (r1 == 0.0f) && (fabsf(v[j]) >= 0x1p-100f);
-          qx[j] = q1;
-        }
+        const float q0 = v[j] * rc;
+        const float r0 = __builtin_fmaf(-q0, sdec, v[j]);
+        const float q1 = __builtin_fmaf(r0, rc, q0);
+        const float r1 = __builtin_fmaf(-q1, sdec, v[j]);
+        const bool amb = ((diff >> (4 * j)) & 15u) != 0u;
+        const bool exact = (r1 == 0.0f) && (fabsf(v[j]) >= 0x1p-100f);
+        ok = ok && (!amb || exact);
+        qx[j] = amb ? q1 : lo[j];
       }
       if (ok) return rtn8_unit(qx);
     }
@@ -255,7 +256,7 @@ __device__ __forceinline__ void mx_dequant_octet_hw(uint32_t w, uint32_t b, void
   }
 }
 
-template <bool BF16OUT, bool MX, int U = 2>
+template <bool BF16OUT, bool MX, int U = 1>
 __global__ __launch_bounds__(kThreads) void dequantize_kernel(
     const uint32_t* __restrict__ packed, const uint8_t* __restrict__ scales,
     const float* __restrict__ st_ptr, int64_t n_oct, void* __restrict__ y) {
@@ -266,7 +267,9 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(
   for (int k = 0; k < U; ++k) {
     const int64_t i = base + (int64_t)k * kThreads;
     const bool ok = i < n_oct;
-    w[k] = ok ? __builtin_nontemporal_load(packed + i) : 0u;
+    // plain (temporal) loads: for 4-byte code loads they stream faster than
+    // non-temporal ones on gfx950
+    w[k] = ok ? packed[i] : 0u;
     b[k] = ok ? scales[i >> (MX ? 2 : 1)] : 0u;
   }
 #pragma unroll
@@ -531,7 +534,7 @@ extern "C" int fp4_dequantize(const uint8_t* packed, const uint8_t* scales,
   hipStream_t st = as_stream(stream);
   const int64_t n_oct = n / 8;
   if (!grid_fits(n_oct)) return FP4_ESHAPE;
-  const dim3 g((unsigned)blocks_for(n_oct, 2));
+  const dim3 g((unsigned)blocks_for(n_oct, 1));
   const uint32_t* pk = reinterpret_cast<const uint32_t*>(packed);
   if (out_dtype == FP4_DTYPE_BF16) {
     if (mx) hipLaunchKernelGGL((dequantize_kernel<true, true>), dim3(g), dim3(kThreads), 0, st, pk, scales, tensor_scale, n_oct, y);

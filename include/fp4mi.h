@@ -182,7 +182,7 @@ int fp4_errfeedback_qdq(const void* x, int dtype, int64_t rows, int64_t cols,
  *  scales_e8m0    [T, H/32] UE8M0 bytes (0xFF outside the contract), 4-byte aligned
  *  token_offsets  device int64 [E+1]: off[0] = 0, nondecreasing, off[E] = T,
  *                 8-byte aligned (contents are not validated on the host)
- *  num_experts    E >= 1;  total_tokens T >= 0;  hidden H > 0, H % 128 == 0
+ *  num_experts    E >= 1;  total_tokens 0 <= T < 2^26;  hidden 0 < H < 2^21, H % 128 == 0
  *  fp8_out        out bytes [T*H]; expert e occupies [H*off[e], H*off[e+1])
  *                 as a dense [H, n_e] matrix
  *  fp8_scales     out fp32 [T*H/128]; expert e occupies

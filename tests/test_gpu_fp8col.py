@@ -28,6 +28,8 @@ def convert_gpu(m, packed, sb, off, H):
     ([0, 0, 1], 128),
     ([64, 64, 64], 256),
     ([200], 7168),
+    ([1009, 3, 2020, 0, 1007, 4, 1], 256),               # pieces across token chunks
+    ([5001], 128),
 ])
 def test_small_ragged_from_quantized_activations(counts, H):
     m = need_gpu()
