@@ -19,7 +19,7 @@ sample, and a breakdown of the other operations of the codec at their own
 workload shapes.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-breakdown]
-                       [--no-cpu-baseline] [--profile-mode {headline,copy}]
+                       [--no-cpu-baseline] [--cpu-seconds S] [--profile-mode {headline,copy}]
        python bench.py --summarize-trace DIR --out FILE --command CMD
        python bench.py --summarize-pmc F_HEAD,F_COPY,W_HEAD,W_COPY --out FILE --command CMD
 """
@@ -272,20 +272,33 @@ def breakdown(args, torch, fp4, np, synth):
 
 
 # ---------------------------------------------------------- cpu baseline
-def cpu_baseline(xb, rows_sample):
+def cpu_baseline(xb, rows_chunk=512, min_seconds=10.0, max_seconds=30.0):
+    """The oracle, untuned, on the host: quantize+dequantize of the headline
+    input in chunks of `rows_chunk` rows, passing over the whole tensor until
+    at least `min_seconds` of work (stopping early past `max_seconds`)."""
     sys.path.insert(0, ROOT)
-    import numpy as np
     from oracle import formats as F
     from oracle import mxfp4
-    x = F.bf16_bits_to_f32(xb[:rows_sample])
-    n = x.size
-    t = time.perf_counter()
-    p, s = mxfp4.quantize_packed(x)
-    mxfp4.dequantize(p, s, "bf16")
-    dt = time.perf_counter() - t
-    nbytes = 2 * (2 * n + n // 2 + n // 32)
+    rows_total = xb.shape[0]
+    nbytes = 0
+    rows_done = 0
+    t0 = time.perf_counter()
+    while True:
+        for r0 in range(0, rows_total, rows_chunk):
+            x = F.bf16_bits_to_f32(xb[r0:r0 + rows_chunk])
+            p, s = mxfp4.quantize_packed(x)
+            mxfp4.dequantize(p, s, "bf16")
+            n = x.size
+            nbytes += 2 * (2 * n + n // 2 + n // 32)
+            rows_done += x.shape[0]
+            if time.perf_counter() - t0 > max_seconds:
+                break
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or dt > max_seconds:
+            break
     return {"value": round(nbytes / dt / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {rows_sample} of 4096 rows ({n} elements) of the same input, "
+            "sample": f"{rows_done} rows ({rows_done / rows_total:.2f} passes over the "
+                      f"{rows_total}x{xb.shape[1]} input, {rows_chunk}-row chunks), "
                       f"quantize+dequantize, {dt:.1f} s single-threaded numpy"}
 
 
@@ -356,8 +369,9 @@ def summarize_pmc(dirs, out, command):
     fetch, write = per_kernel(fh, "FETCH_SIZE"), per_kernel(wh, "WRITE_SIZE")
     n = 4096 * 7168
     alg = 2 * n + n // 2 + n // 32
-    q = "quantize_kernel<true, true, false>"
-    d = "dequantize_kernel<true, true>"
+    # template arguments: <bf16 input, MX, SR, ...> and <bf16 output, MX, ...>
+    q = next(k for k in fetch if k.startswith("quantize_kernel<true, true, false"))
+    d = next(k for k in fetch if k.startswith("dequantize_kernel<true, true"))
     lines = ["# rocprofv3 PMC summary: HBM traffic of the MXFP4 headline kernels (4096x7168 bf16)",
              f"# command: {command}",
              f"# copy calibration: FETCH_SIZE reads {f_copy:.0f} B for a {copy_bytes} B copy (x{kf:.4f}); "
@@ -384,7 +398,8 @@ def main():
     ap.add_argument("--breakdown-iters", type=int, default=30)
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum oracle time for the cpu_baseline leg")
     ap.add_argument("--profile-mode", choices=["headline", "copy"])
     ap.add_argument("--summarize-pmc", help="FETCH_headline,FETCH_copy,WRITE_headline,WRITE_copy dirs")
     ap.add_argument("--summarize-trace", help="rocprofv3 --kernel-trace output dir")
@@ -451,8 +466,8 @@ def main():
     if not args.no_breakdown:
         res["breakdown"] = breakdown(args, torch, fp4, np, synth)
     if not args.no_cpu_baseline:
-        log(f"[bench] cpu baseline: oracle on {args.cpu_rows} rows")
-        res["cpu_baseline"] = cpu_baseline(h["xb"], args.cpu_rows)
+        log(f"[bench] cpu baseline: oracle for at least {args.cpu_seconds:.0f} s")
+        res["cpu_baseline"] = cpu_baseline(h["xb"], min_seconds=args.cpu_seconds)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)
