@@ -40,19 +40,25 @@ __device__ __forceinline__ NvScale nv_block_scale_exact(float absmax, float st) 
 // a normal number, r' = absmax * kinv is within 2^-21 (relative) of
 // fl32(fl32(absmax/6)/S_t); E4M3 encoding is monotone, so if r'(1 - 2^-18)
 // and r'(1 + 2^-18) encode to the same byte the exact quotient does too.
-// Otherwise (a quotient within 2^-18 of an E4M3 rounding boundary) the
-// divisions are done.
+// Otherwise (a quotient within 2^-18 of an E4M3 rounding boundary) *sure is
+// cleared and the exact scale must be taken instead.
+__device__ __forceinline__ NvScale nv_block_scale_fast(float absmax, float st, float kinv,
+                                                       bool* sure) {
+  const float r = absmax * kinv;
+  const uint32_t lo = e4m3_encode_sat_hw(r * 0x1.fffcp-1f);     // 1 - 2^-18
+  const uint32_t hi = e4m3_encode_sat_hw(r * 0x1.00004p+0f);    // 1 + 2^-18
+  *sure = lo == hi;
+  NvScale s;
+  s.code = lo;
+  s.sdec = e4m3_value(lo) * st;
+  return s;
+}
+
 __device__ __forceinline__ NvScale nv_block_scale(float absmax, float st, float kinv, bool fast) {
   if (fast) {
-    const float r = absmax * kinv;
-    const uint32_t lo = e4m3_encode_sat_hw(r * 0x1.fffcp-1f);     // 1 - 2^-18
-    const uint32_t hi = e4m3_encode_sat_hw(r * 0x1.00004p+0f);    // 1 + 2^-18
-    if (lo == hi) {
-      NvScale s;
-      s.code = lo;
-      s.sdec = e4m3_value(lo) * st;
-      return s;
-    }
+    bool sure;
+    const NvScale s = nv_block_scale_fast(absmax, st, kinv, &sure);
+    if (sure) return s;
   }
   return nv_block_scale_exact(absmax, st);
 }
@@ -85,6 +91,16 @@ __device__ __forceinline__ void unpack_f32x8(const u32x4& a, const u32x4& b, flo
   v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
   v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y);
   v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+}
+
+template <bool BF16>
+__device__ __forceinline__ void load_octet(const void* x, int64_t i, float (&v)[8]) {
+  if constexpr (BF16) {
+    unpack_bf16x8(ld_u32x4(static_cast<const uint8_t*>(x) + i * 16), v);
+  } else {
+    const uint8_t* p = static_cast<const uint8_t*>(x) + i * 32;
+    unpack_f32x8(ld_u32x4(p), ld_u32x4(p + 16), v);
+  }
 }
 
 // Codes of one octet under a decided block scale (software rounding; exact).
@@ -122,47 +138,64 @@ __device__ __forceinline__ uint32_t encode_octet_sw(const float (&v)[8], float s
 // monotone in |q|, so when both round to the same code so does
 // fl32(v / sdec).  Otherwise (an element within ~2^-18 of a rounding
 // threshold) the octet is redone with IEEE divisions.
-__device__ __forceinline__ uint32_t encode_octet_nv_rtn(const float (&v)[8], float sdec, int64_t i) {
-  if (sdec >= 0x1p-125f && sdec <= 0x1p+125f) {
-    const float rc = __builtin_amdgcn_rcpf(sdec);
-    const float rlo = rc * 0x1.fffcp-1f;      // (1/sdec)(1 - 2^-18), within 2^-22
-    const float rhi = rc * 0x1.00004p+0f;     // (1/sdec)(1 + 2^-18), within 2^-22
-    float lo[8], hi[8];
+__device__ __forceinline__ uint32_t encode_octet_nv_rtn_fast(const float (&v)[8], float sdec,
+                                                             bool* sure) {
+  *sure = false;
+  if (!(sdec >= 0x1p-125f && sdec <= 0x1p+125f)) return 0u;
+  const float rc = __builtin_amdgcn_rcpf(sdec);
+  const float rlo = rc * 0x1.fffcp-1f;      // (1/sdec)(1 - 2^-18), within 2^-22
+  const float rhi = rc * 0x1.00004p+0f;     // (1/sdec)(1 + 2^-18), within 2^-22
+  float lo[8], hi[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      lo[j] = v[j] * rlo;
-      hi[j] = v[j] * rhi;
-    }
-    const uint32_t wl = rtn8_unit(lo), wh = rtn8_unit(hi);
-    if (wl == wh) return wl;
-    // Some element sits within 2^-18 of a threshold.  Exact quotients are
-    // common there (short binary fractions over short scales), so refine
-    // each such element with one correction step and accept it when the
-    // remainder fma(-q1, sdec, v) is exactly zero, i.e. q1 * sdec == v and
-    // fl32(v / sdec) == q1.  With sdec in [2^-60, 2^60], |v| >= 2^-100 and
-    // |q1| near a threshold, a nonzero remainder is a multiple of 2^-123
-    // and cannot round to zero.
-    if (sdec >= 0x1p-60f && sdec <= 0x1p+60f) {
-      // branch-free over the octet: elements whose bracket agreed keep that
-      // code (through lo); the others must be certified exact
-      const uint32_t diff = wl ^ wh;
-      bool ok = true;
-      float qx[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float q0 = v[j] * rc;
-        const float r0 = __builtin_fmaf(-q0, sdec, v[j]);
-        const float q1 = __builtin_fmaf(r0, rc, q0);
-        const float r1 = __builtin_fmaf(-q1, sdec, v[j]);
-        const bool amb = ((diff >> (4 * j)) & 15u) != 0u;
-        const bool exact = (r1 == 0.0f) && (fabsf(v[j]) >= 0x1p-100f);
-        ok = ok && (!amb || exact);
-        qx[j] = amb ? q1 : lo[j];
-      }
-      if (ok) return rtn8_unit(qx);
-    }
+  for (int j = 0; j < 8; ++j) {
+    lo[j] = v[j] * rlo;
+    hi[j] = v[j] * rhi;
   }
-  return encode_octet_sw<false, false>(v, sdec, 0, i, 0, 0);
+  const uint32_t wl = rtn8_unit(lo), wh = rtn8_unit(hi);
+  if (wl == wh) {
+    *sure = true;
+    return wl;
+  }
+  // Some element sits within 2^-18 of a threshold (exact quotients are
+  // common there: short binary fractions over short scales).  Those elements
+  // take one correction step from a Newton-refined reciprocal, q1 =
+  // q0 + fma(-q0, sdec, v) / sdec, and q1 is accepted as fl32(v / sdec) when
+  // the remainder r1 = fma(-q1, sdec, v) satisfies |r1| < ulp(q1) / 2 * sdec,
+  // i.e. |v / sdec - q1| < ulp(q1) / 2 (a quarter ulp when q1 is a power of
+  // two), so that q1 rounds it to nearest (if q1 is within an ulp of the
+  // quotient the remainder is exact; if it is farther, |r1| is at least
+  // ulp(q1) sdec and no rounding brings it below the bound).  With sdec in
+  // [2^-60, 2^60] and |q1| >= 0.25 near a threshold the bound is a normal
+  // number.  An element that fails the test leaves *sure false.
+  if (!(sdec >= 0x1p-60f && sdec <= 0x1p+60f)) return 0u;
+  const float rc2 = __builtin_fmaf(__builtin_fmaf(-sdec, rc, 1.0f), rc, rc);
+  const uint32_t diff = wl ^ wh;
+  bool ok = true;
+  float qx[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float q0 = v[j] * rc2;
+    const float r0 = __builtin_fmaf(-q0, sdec, v[j]);
+    const float q1 = __builtin_fmaf(r0, rc2, q0);
+    const float r1 = __builtin_fmaf(-q1, sdec, v[j]);
+    const int eb = (int)((__float_as_uint(q1) >> 23) & 0xFFu);          // biased exponent
+    // ulp(q1)/2 * sdec, or a quarter ulp when q1 is a power of two (the
+    // spacing below it is half as wide)
+    const int pow2 = (__float_as_uint(q1) & 0x7FFFFFu) == 0u ? 1 : 0;
+    const float bound = __builtin_amdgcn_ldexpf(sdec, eb - 151 - pow2);
+    const bool amb = ((diff >> (4 * j)) & 15u) != 0u;
+    ok = ok && (!amb || (fabsf(r1) < bound && eb >= 125));
+    qx[j] = amb ? q1 : lo[j];
+  }
+  *sure = ok;
+  return rtn8_unit(qx);
+}
+
+// The same codes, exact in every case (IEEE divisions when unsure).
+__device__ __forceinline__ uint32_t encode_octet_nv_rtn(const float (&v)[8], float sdec, int64_t i) {
+  bool sure;
+  const uint32_t w = encode_octet_nv_rtn_fast(v, sdec, &sure);
+  return sure ? w : encode_octet_sw<false, false>(v, sdec, 0, i, 0, 0);
 }
 
 // MXFP4 RTN codes: divide by 2^e and round in the converter (bf16 words go
@@ -197,6 +230,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
   bool fast = false;
   const float kinv = MX ? 0.0f : nv_kinv(st, &fast);
   const int64_t base = (int64_t)blockIdx.x * (kThreads * U) + threadIdx.x;
+  uint32_t redo = 0;   // NVFP4 RTN: octets to redo exactly
   u32x4 ra[U], rb[U];
 #pragma unroll
   for (int k = 0; k < U; ++k) {
@@ -224,15 +258,43 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
       scode = mx_scale_byte(am);
       if constexpr (SR) word = encode_octet_sw<true, true>(v, 0.0f, 127 - (int)scode, i, seed, step);
       else word = encode_octet_mx_rtn<BF16>(ra[k], v, scode);
-    } else {
+    } else if constexpr (SR) {
       const NvScale s = nv_block_scale(am, st, kinv, fast);
       scode = s.code;
-      if constexpr (SR) word = encode_octet_sw<false, true>(v, s.sdec, 0, i, seed, step);
-      else word = encode_octet_nv_rtn(v, s.sdec, i);
+      word = encode_octet_sw<false, true>(v, s.sdec, 0, i, seed, step);
+    } else {
+      // codes without divisions; an octet they cannot certify is redone
+      // with IEEE divisions after the loop
+      const NvScale s = nv_block_scale(am, st, kinv, fast);
+      scode = s.code;
+      bool sure = false;
+      word = encode_octet_nv_rtn_fast(v, s.sdec, &sure);
+      if (!sure) {
+        redo |= 1u << k;
+        if (i < n_oct && (i & 1) == 0) scales[i >> 1] = (uint8_t)scode;
+        continue;
+      }
     }
     if (i < n_oct) {
       st_u32(packed + i, word);
       if ((i & (MX ? 3 : 1)) == 0) scales[i >> (MX ? 2 : 1)] = (uint8_t)scode;
+    }
+  }
+  if constexpr (!MX && !SR) {
+    // Octets whose codes were not certain: redone with IEEE divisions, out
+    // of the hot loop (the block scale, already stored, is recomputed from
+    // the octet and its block partner).
+    while (redo) {
+      const int k = __builtin_ctz(redo);
+      redo &= redo - 1;
+      const int64_t i = base + (int64_t)k * kThreads;
+      if (i >= n_oct) continue;
+      float v[8], w[8];
+      load_octet<BF16>(x, i, v);
+      load_octet<BF16>(x, i ^ 1, w);                     // the block partner (n_oct is even)
+      const float am = fmaxf(absmax8(v), absmax8(w));
+      const NvScale s = nv_block_scale_exact(am, st);
+      st_u32(packed + i, encode_octet_sw<false, false>(v, s.sdec, 0, i, 0, 0));
     }
   }
 }

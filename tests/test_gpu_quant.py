@@ -129,6 +129,33 @@ def test_nvfp4_unit_scale_fp32_threshold_neighbourhood():
             np.testing.assert_array_equal(s, rs)
 
 
+def test_nvfp4_bf16_input_exact_and_ambiguous_quotients():
+    """bf16 input (the octets the exact redo reloads as bf16): values at and
+    next to every threshold and grid point, both signs, in blocks of absmax 6,
+    under given tensor scales that make x / s_dec an exact tie (S_t = 1), a
+    quotient 2^-20 off a threshold (S_t = 1 + 2^-20: ambiguous for the
+    reciprocal bracket, not exact), and a subnormal S_t (no fast scale)."""
+    m = need_gpu()
+    vals = []
+    for t in (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0):
+        b = int(F.f32_to_bf16_bits(np.array([t], np.float32))[0])
+        for k in range(-2, 3):
+            vals += [b + k, (b + k) | 0x8000]
+    v = F.bf16_bits_to_f32(np.array(vals, np.uint16))
+    v = np.concatenate([v, np.zeros((-v.size) % 15, np.float32)]).reshape(-1, 15)
+    blk = np.concatenate([np.full((v.shape[0], 1), 6.0, np.float32), v], axis=1)
+    blk = np.concatenate([blk] * 4, axis=0).reshape(4, -1)
+    bits = F.f32_to_bf16_bits(blk)
+    assert np.array_equal(F.bf16_bits_to_f32(bits), blk)          # exactly representable
+    for st in (np.float32(1.0), np.float32(1.0 + 2.0 ** -20), np.float32(2.0 ** -140),
+               np.float32(0.37)):
+        ts = dev_f32(np.array([st], np.float32))
+        p, s, _ = run_quant(m, dev_bf16(bits), "nvfp4", tscale="given", ts=ts)
+        rp, rs = nvfp4.quantize_packed(blk, st)
+        np.testing.assert_array_equal(s, rs)
+        np.testing.assert_array_equal(p, rp)
+
+
 def test_nvfp4_dequantize_foreign_scale_bytes():
     """Dequantize accepts any E4M3 byte (signed, subnormal, NaN) and code."""
     m = need_gpu()
