@@ -212,6 +212,426 @@ __global__ __launch_bounds__(kThreads) void fp4quant_decode_kernel(
   }
 }
 
+// ------------------------------------------- row layout (G <= 256)
+// A wavefront converts a tile of 512 consecutive octets (4096 elements).
+// Global memory sees only whole-tile streams: every load and store
+// instruction moves 64 consecutive 16-byte chunks (1 KiB).  The tile passes
+// through the wave's own LDS, where it is regrouped: the G / 8 octets of a
+// group go to LPG lanes (1, 2 or 4) that lie D = 64 / LPG lanes apart (the
+// same lane of different 32- or 16-lane rows), S = min(G / 8, 8) octets per
+// lane, and a lane handles U groups in turn (512 octets = U * 64 * S).
+// Every butterfly stage then runs inside a lane: stages over the element
+// bits of an octet and over the octet bits a lane holds are register
+// butterflies; the stage over a row bit of the octet index first exchanges
+// that bit with a slot bit through the gfx950 row-swap instructions
+// (v_permlane16_swap: rows 0<->1 and 2<->3 of 16 lanes; v_permlane32_swap:
+// the two 32-lane halves), after which the two octets that differ in the row
+// bit sit in one lane.  No select and no cross-lane shuffle through LDS.
+//
+// Octet index o within a group (bits: LPG row bits r, then slot bits s):
+//   layout L0 (the encoder's input, the decoder's output): o = r + LPG s;
+//   layout P  (the encoder's codes, the decoder's input): row bit k of o is
+//     slot bit C_k of the register and slot bit C_k of o is row bit k of the
+//     lane.  In P a lane holds runs of 4 (G = 16: 2) consecutive octets,
+//     whose codes are one 16-byte (8-byte) LDS word.
+// LDS chunks (16 bytes) are XOR-swizzled, chunk c at c ^ ((c >> sh) & 7),
+// so that the 8 lanes served together by a 16-byte LDS access hit 8
+// different bank quads both for the linear (global-side) and the grouped
+// (compute-side) access.
+template <int G> struct RowCfg;
+template <> struct RowCfg<16> { static constexpr int LPG = 1, S = 2, C0 = 0, C1 = 0; };
+template <> struct RowCfg<32> { static constexpr int LPG = 1, S = 4, C0 = 0, C1 = 0; };
+template <> struct RowCfg<64> { static constexpr int LPG = 1, S = 8, C0 = 0, C1 = 0; };
+template <> struct RowCfg<128> { static constexpr int LPG = 2, S = 8, C0 = 1, C1 = 0; };
+template <> struct RowCfg<256> { static constexpr int LPG = 4, S = 8, C0 = 0, C1 = 1; };
+
+constexpr int kTileOct = 512;                 // octets per wave tile
+constexpr int kRowWaves = 4;                  // waves per workgroup
+
+// Octet (within the group) of row r, slot s in layout P.
+template <class C>
+__host__ __device__ constexpr int oct_p(int r, int s) {
+  int rr = 0, ss = s;
+  if (C::LPG >= 2) {
+    rr |= (s >> C::C0) & 1;
+    ss = (ss & ~(1 << C::C0)) | ((r & 1) << C::C0);
+  }
+  if (C::LPG >= 4) {
+    rr |= ((s >> C::C1) & 1) << 1;
+    ss = (ss & ~(1 << C::C1)) | (((r >> 1) & 1) << C::C1);
+  }
+  return rr + C::LPG * ss;
+}
+template <class C> constexpr int kRun = C::S < 4 ? C::S : 4;     // octets per run in P
+// The slot holding the octet whose row-0 index in layout P is o0.
+template <class C>
+__host__ __device__ constexpr int slot_of_p(int o0) {
+  for (int s = 0; s < C::S; ++s)
+    if (oct_p<C>(0, s) == o0) return s;
+  return -1;
+}
+// The slot that starts the j-th run in layout P.
+template <class C>
+__host__ __device__ constexpr int run_start_slot(int j) {
+  for (int s = 0; s < C::S; ++s)
+    if (oct_p<C>(0, s) % kRun<C> == 0 && j-- == 0) return s;
+  return -1;
+}
+constexpr int ilog2c(int v) { return v <= 1 ? 0 : 1 + ilog2c(v / 2); }
+// Swizzled position of chunk c when a group spans `span` chunks.
+template <int SPAN>
+__device__ __forceinline__ int swz_chunk(int c) {
+  constexpr int sh = ilog2c(SPAN) > 3 ? ilog2c(SPAN) : 3;
+  return c ^ ((c >> sh) & 7);
+}
+
+__device__ __forceinline__ void swap16(float& a, float& b) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  a = __uint_as_float(p[0]);
+  b = __uint_as_float(p[1]);
+}
+__device__ __forceinline__ void swap32(float& a, float& b) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  a = __uint_as_float(p[0]);
+  b = __uint_as_float(p[1]);
+}
+// Exchange of row bit k with slot bit C_k for every slot pair, then the
+// butterfly over the pair (now the stage over row bit k of the octet index).
+template <class C, int K, int S>
+__device__ __forceinline__ void row_stage(float (&v)[S][8]) {
+  constexpr int h = 1 << (K == 0 ? C::C0 : C::C1);
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    if (s & h) continue;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float a = v[s][j], b = v[s | h][j];
+      if constexpr (C::LPG == 4 && K == 0) swap16(a, b);
+      else swap32(a, b);
+      v[s][j] = a + b;
+      v[s | h][j] = a - b;
+    }
+  }
+}
+// Register butterflies over the 8 elements of each octet and over the slot bits.
+template <int S>
+__device__ __forceinline__ void wht_in_lane(float (&v)[S][8]) {
+#pragma unroll
+  for (int s = 0; s < S; ++s) wht_local<8>(v[s]);
+#pragma unroll
+  for (int h = 1; h < S; h <<= 1) {
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      if (s & h) continue;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float a = v[s][j], b = v[s | h][j];
+        v[s][j] = a + b;
+        v[s | h][j] = a - b;
+      }
+    }
+  }
+}
+// Sum / max over the LPG lanes of a group (a row swap of a value with itself
+// gives every lane its partner row's value in one of the two results).
+template <int LPG>
+__device__ __forceinline__ float rows_sum(float x) {
+  if constexpr (LPG == 4) { float a = x, b = x; swap16(a, b); x = a + b; }
+  if constexpr (LPG >= 2) { float a = x, b = x; swap32(a, b); x = a + b; }
+  return x;
+}
+template <int LPG>
+__device__ __forceinline__ float rows_max(float x) {
+  if constexpr (LPG == 4) { float a = x, b = x; swap16(a, b); x = fmaxf(a, b); }
+  if constexpr (LPG >= 2) { float a = x, b = x; swap32(a, b); x = fmaxf(a, b); }
+  return x;
+}
+// Sum of squares of the lane's elements (short fma chains, then a tree).
+template <int S>
+__device__ __forceinline__ float lane_sumsq(const float (&v)[S][8]) {
+  float t[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    float a = v[s][0] * v[s][0], b = v[s][4] * v[s][4];
+#pragma unroll
+    for (int j = 1; j < 4; ++j) {
+      a = __builtin_fmaf(v[s][j], v[s][j], a);
+      b = __builtin_fmaf(v[s][4 + j], v[s][4 + j], b);
+    }
+    t[s] = a + b;
+  }
+#pragma unroll
+  for (int h = 1; h < S; h <<= 1)
+#pragma unroll
+    for (int s = 0; s < S; s += 2 * h) t[s] = t[s] + t[s + h];
+  return t[0];
+}
+template <int S>
+__device__ __forceinline__ float lane_absmax(const float (&v)[S][8]) {
+  float m = 0.0f;
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) m = fmaxf(m, fmaxf(fabsf(v[s][j]), fabsf(v[s][j + 1])));
+  return m;
+}
+
+// Orders the wave's LDS accesses: writes by some lanes before reads of the
+// same bytes by others.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
+// Encoder arithmetic as above (codes 6 w / max|w|, s2 = max|w| / (6 sqrt(ss)),
+// s1 = sqrt(ss / G)), with the approximate reciprocal and square-root
+// instructions: this path is checked against the oracle within a tolerance,
+// and their error (about 1 ulp each) stays far inside it.  A group whose sum
+// of squares leaves [2^-100, 2^126) (tiny, huge or zero groups) is first
+// scaled by a power of two that brings its largest element to [1, 2): the
+// codes and s2 do not change under such scaling, s1 is scaled back exactly.
+template <bool BF16, int G>
+__global__ __launch_bounds__(64 * kRowWaves) void fq_encode_rows_kernel(
+    const void* __restrict__ x, int64_t n_oct, uint32_t* __restrict__ packed,
+    float* __restrict__ s_rms, float* __restrict__ s_abs) {
+  using C = RowCfg<G>;
+  constexpr int LPG = C::LPG, S = C::S, D = 64 / LPG, NO = G / 8;
+  constexpr int U = kTileOct / (D * NO);             // groups a lane handles in turn
+  constexpr int NW = BF16 ? 1 : 2;                   // 16-byte chunks per octet
+  constexpr int TCH = kTileOct * NW;                 // input chunks per tile
+  __shared__ u32x4 tile_in[kRowWaves][TCH];
+  __shared__ u32x4 tile_codes[kRowWaves][kTileOct / 4];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int gw = lane % D, r = lane / D;
+  const int64_t wave = (int64_t)blockIdx.x * kRowWaves + wv;
+  const int64_t t0 = wave * kTileOct;                // first octet of the tile
+  u32x4* lin = tile_in[wv];
+  u32x4* lcodes = tile_codes[wv];
+
+  // 1. the tile, linear 1 KiB streams -> LDS (chunks past the end read chunk 0)
+  {
+    const int64_t nch = n_oct * NW, c0 = t0 * NW;
+    u32x4 a[TCH / 64];
+#pragma unroll
+    for (int k = 0; k < TCH / 64; ++k) {
+      const int64_t c = c0 + 64 * k + lane;
+      a[k] = ld_u32x4(static_cast<const uint8_t*>(x) + (c < nch ? c : 0) * 16);
+    }
+#pragma unroll
+    for (int k = 0; k < TCH / 64; ++k) lin[swz_chunk<NO * NW>(64 * k + lane)] = a[k];
+  }
+  wave_lds_sync();
+
+#pragma unroll 1
+  for (int u = 0; u < U; ++u) {
+    const int gl = u * D + gw;                       // group within the tile
+    const int64_t g = t0 / NO + gl;
+    // 2. the group's octets, layout L0
+    float v[S][8];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const int c = (gl * NO + r + LPG * s) * NW;
+      const u32x4 p = lin[swz_chunk<NO * NW>(c)];
+      if constexpr (BF16) {
+        v[s][0] = bf16_lo(p.x); v[s][1] = bf16_hi(p.x); v[s][2] = bf16_lo(p.y); v[s][3] = bf16_hi(p.y);
+        v[s][4] = bf16_lo(p.z); v[s][5] = bf16_hi(p.z); v[s][6] = bf16_lo(p.w); v[s][7] = bf16_hi(p.w);
+      } else {
+        const u32x4 q = lin[swz_chunk<NO * NW>(c + 1)];
+        v[s][0] = __uint_as_float(p.x); v[s][1] = __uint_as_float(p.y);
+        v[s][2] = __uint_as_float(p.z); v[s][3] = __uint_as_float(p.w);
+        v[s][4] = __uint_as_float(q.x); v[s][5] = __uint_as_float(q.y);
+        v[s][6] = __uint_as_float(q.z); v[s][7] = __uint_as_float(q.w);
+      }
+    }
+    // 3. scales and codes
+    float ss = rows_sum<LPG>(lane_sumsq<S>(v));
+    int e = 0;
+    const bool odd = !(ss >= 0x1p-100f && ss < 0x1p+126f);
+    if (__builtin_amdgcn_ballot_w64(odd)) {          // rare: some group of the wave
+      const float mxx = rows_max<LPG>(lane_absmax<S>(v));
+      e = (odd && mxx > 0.0f) ? __builtin_amdgcn_frexp_expf(mxx) - 1 : 0;
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[s][j] = __builtin_amdgcn_ldexpf(v[s][j], -e);
+      ss = rows_sum<LPG>(lane_sumsq<S>(v));
+    }
+    wht_in_lane<S>(v);
+    if constexpr (LPG >= 2) row_stage<C, 0>(v);
+    if constexpr (LPG >= 4) row_stage<C, 1>(v);
+    const float mx = rows_max<LPG>(lane_absmax<S>(v));
+    const bool zero = !(mx > 0.0f) || !(ss > 0.0f);
+    const float rq = zero ? 0.0f : 6.0f * __builtin_amdgcn_rcpf(mx);
+    const uint32_t keep = zero ? 0u : ~0u;             // a zero group's codes are 0
+    uint32_t w[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      float q[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) q[j] = v[s][j] * rq;
+      w[s] = rtn8_unit(q) & keep;
+    }
+    // codes -> LDS in runs (layout P); word index = gl * NO + octet
+#pragma unroll
+    for (int jr = 0; jr < S / kRun<C>; ++jr) {
+      constexpr int RL = kRun<C>;
+      const int s0 = run_start_slot<C>(jr);
+      const int o0 = oct_p<C>(0, s0);
+      const int wi = gl * NO + oct_p<C>(r, s0);
+      uint8_t* dst = reinterpret_cast<uint8_t*>(lcodes + swz_chunk<1>(wi >> 2)) + 4 * (wi & 3);
+      if constexpr (RL == 4) {
+        *reinterpret_cast<u32x4*>(dst) = u32x4{w[slot_of_p<C>(o0)], w[slot_of_p<C>(o0 + 1)],
+                                               w[slot_of_p<C>(o0 + 2)], w[slot_of_p<C>(o0 + 3)]};
+      } else {
+        *reinterpret_cast<u32x2*>(dst) = u32x2{w[slot_of_p<C>(o0)], w[slot_of_p<C>(o0 + 1)]};
+      }
+    }
+    if (r == 0 && g * NO < n_oct) {
+      const float s1 = __builtin_amdgcn_sqrtf(ss * (1.0f / (float)G));
+      const float s2 = (mx * __builtin_amdgcn_rsqf(ss)) * (1.0f / 6.0f);
+      s_rms[g] = zero ? 0.0f : __builtin_amdgcn_ldexpf(s1, e);
+      s_abs[g] = zero ? 0.0f : s2;
+    }
+  }
+  wave_lds_sync();
+  // 4. codes, linear 1 KiB streams (a chunk the end cuts in two: its 2 valid words)
+#pragma unroll
+  for (int k = 0; k < kTileOct / 4 / 64; ++k) {
+    const int c = 64 * k + lane;
+    const int64_t w0 = t0 + 4 * c;
+    const u32x4 q = lcodes[swz_chunk<1>(c)];
+    if (w0 + 4 <= n_oct) st_u32x4(packed + w0, q);
+    else if (w0 < n_oct) __builtin_nontemporal_store(u32x2{q.x, q.y}, reinterpret_cast<u32x2*>(packed + w0));
+  }
+}
+
+// Receiver: codes in layout P, output in layout L0.  2 e2m1 values are
+// integers in [-12, 12] and every partial sum of the transform an integer
+// below 2^13, so the fp32 butterflies are exact; one multiply by
+// s1 s2 / (2 sqrt(G)) per element follows.
+template <bool BF16OUT, int G>
+__global__ __launch_bounds__(64 * kRowWaves) void fq_decode_rows_kernel(
+    const uint32_t* __restrict__ packed, const float* __restrict__ s_rms,
+    const float* __restrict__ s_abs, int64_t n_oct, float c_dec, void* __restrict__ y) {
+  using C = RowCfg<G>;
+  constexpr int LPG = C::LPG, S = C::S, D = 64 / LPG, NO = G / 8;
+  constexpr int U = kTileOct / (D * NO);
+  constexpr int NW = BF16OUT ? 1 : 2;                // 16-byte output chunks per octet
+  constexpr int TCH = kTileOct * NW;
+  __shared__ u32x4 tile_out[kRowWaves][TCH];
+  __shared__ u32x4 tile_codes[kRowWaves][kTileOct / 4];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int gw = lane % D, r = lane / D;
+  const int64_t wave = (int64_t)blockIdx.x * kRowWaves + wv;
+  const int64_t t0 = wave * kTileOct;
+  u32x4* lout = tile_out[wv];
+  u32x4* lcodes = tile_codes[wv];
+
+  // 1. codes, linear 1 KiB streams -> LDS
+  {
+    u32x4 a[kTileOct / 4 / 64];
+#pragma unroll
+    for (int k = 0; k < kTileOct / 4 / 64; ++k) {
+      const int64_t w0 = t0 + 4 * (64 * k + lane);
+      if (w0 + 4 <= n_oct) {
+        a[k] = *reinterpret_cast<const u32x4*>(packed + w0);
+      } else {
+        const u32x2 h = w0 < n_oct ? *reinterpret_cast<const u32x2*>(packed + w0) : u32x2{0u, 0u};
+        a[k] = u32x4{h.x, h.y, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kTileOct / 4 / 64; ++k) lcodes[swz_chunk<1>(64 * k + lane)] = a[k];
+  }
+  float f[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t g = t0 / NO + u * D + gw;
+    const int64_t gc = g * NO < n_oct ? g : 0;       // past the end: group 0 (not stored)
+    f[u] = (s_rms[gc] * s_abs[gc]) * c_dec;
+  }
+  wave_lds_sync();
+
+#pragma unroll 1
+  for (int u = 0; u < U; ++u) {
+    const int gl = u * D + gw;
+    // 2. the group's codes, layout P
+    uint32_t w[S];
+#pragma unroll
+    for (int jr = 0; jr < S / kRun<C>; ++jr) {
+      constexpr int RL = kRun<C>;
+      const int s0 = run_start_slot<C>(jr);
+      const int o0 = oct_p<C>(0, s0);
+      const int wi = gl * NO + oct_p<C>(r, s0);
+      const uint8_t* src = reinterpret_cast<const uint8_t*>(lcodes + swz_chunk<1>(wi >> 2)) + 4 * (wi & 3);
+      if constexpr (RL == 4) {
+        const u32x4 q = *reinterpret_cast<const u32x4*>(src);
+        w[slot_of_p<C>(o0)] = q.x;
+        w[slot_of_p<C>(o0 + 1)] = q.y;
+        w[slot_of_p<C>(o0 + 2)] = q.z;
+        w[slot_of_p<C>(o0 + 3)] = q.w;
+      } else {
+        const u32x2 q = *reinterpret_cast<const u32x2*>(src);
+        w[slot_of_p<C>(o0)] = q.x;
+        w[slot_of_p<C>(o0 + 1)] = q.y;
+      }
+    }
+    // 3. transform and scale
+    float c[S][8];
+#pragma unroll
+    for (int s = 0; s < S; ++s) e2m1x8_to_f32(w[s], 2.0f, c[s]);
+    wht_in_lane<S>(c);
+    if constexpr (LPG >= 2) row_stage<C, 0>(c);
+    if constexpr (LPG >= 4) row_stage<C, 1>(c);
+    // outputs -> LDS, layout L0
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const int ch = (gl * NO + r + LPG * s) * NW;
+      float o[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[j] = c[s][j] * f[u];
+      if constexpr (BF16OUT) {
+        lout[swz_chunk<NO * NW>(ch)] = u32x4{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
+                                             pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])};
+      } else {
+        lout[swz_chunk<NO * NW>(ch)] = u32x4{__float_as_uint(o[0]), __float_as_uint(o[1]),
+                                             __float_as_uint(o[2]), __float_as_uint(o[3])};
+        lout[swz_chunk<NO * NW>(ch + 1)] = u32x4{__float_as_uint(o[4]), __float_as_uint(o[5]),
+                                                 __float_as_uint(o[6]), __float_as_uint(o[7])};
+      }
+    }
+  }
+  wave_lds_sync();
+  // 4. outputs, linear 1 KiB streams
+  const int64_t nch = n_oct * NW, c0 = t0 * NW;
+#pragma unroll
+  for (int k = 0; k < TCH / 64; ++k) {
+    const int c = 64 * k + lane;
+    if (c0 + c < nch) st_u32x4(static_cast<uint8_t*>(y) + (c0 + c) * 16, lout[swz_chunk<NO * NW>(c)]);
+  }
+}
+
+template <bool BF16, int G>
+void launch_encode_rows(const void* x, int64_t n, uint32_t* pk, float* s1, float* s2,
+                        hipStream_t st) {
+  const int64_t n_oct = n / 8;
+  const int64_t waves = (n_oct + kTileOct - 1) / kTileOct;
+  hipLaunchKernelGGL((fq_encode_rows_kernel<BF16, G>),
+                     dim3((unsigned)((waves + kRowWaves - 1) / kRowWaves)), dim3(64 * kRowWaves), 0,
+                     st, x, n_oct, pk, s1, s2);
+}
+template <bool BF16OUT, int G>
+void launch_decode_rows(const uint32_t* pk, const float* s1, const float* s2, int64_t n, void* y,
+                        hipStream_t st) {
+  const int64_t n_oct = n / 8;
+  const int64_t waves = (n_oct + kTileOct - 1) / kTileOct;
+  const float c_dec = (float)(0.5 / __builtin_sqrt((double)G));
+  hipLaunchKernelGGL((fq_decode_rows_kernel<BF16OUT, G>),
+                     dim3((unsigned)((waves + kRowWaves - 1) / kRowWaves)), dim3(64 * kRowWaves), 0,
+                     st, pk, s1, s2, n_oct, c_dec, y);
+}
+
 template <bool BF16>
 void launch_encode(int G, const void* x, int64_t n, uint32_t* pk, float* s1, float* s2,
                    hipStream_t st) {
@@ -225,11 +645,11 @@ void launch_encode(int G, const void* x, int64_t n, uint32_t* pk, float* s1, flo
                        dim3(kThreads), 0, st, x, nl, inv_g, c_s2, pk, s1, s2);                 \
   }
   switch (G) {
-    case 16: FP4MI_ENC(8, 2); break;
-    case 32: FP4MI_ENC(8, 4); break;
-    case 64: FP4MI_ENC(8, 8); break;
-    case 128: FP4MI_ENC(8, 16); break;
-    case 256: FP4MI_ENC(8, 32); break;
+    case 16: launch_encode_rows<BF16, 16>(x, n, pk, s1, s2, st); break;
+    case 32: launch_encode_rows<BF16, 32>(x, n, pk, s1, s2, st); break;
+    case 64: launch_encode_rows<BF16, 64>(x, n, pk, s1, s2, st); break;
+    case 128: launch_encode_rows<BF16, 128>(x, n, pk, s1, s2, st); break;
+    case 256: launch_encode_rows<BF16, 256>(x, n, pk, s1, s2, st); break;
     case 512: FP4MI_ENC(8, 64); break;
     case 1024: FP4MI_ENC(16, 64); break;
   }
@@ -248,11 +668,11 @@ void launch_decode(int G, const uint32_t* pk, const float* s1, const float* s2, 
                        dim3(kThreads), 0, st, pk, s1, s2, nl, c_dec, y);                      \
   }
   switch (G) {
-    case 16: FP4MI_DEC(8, 2); break;
-    case 32: FP4MI_DEC(8, 4); break;
-    case 64: FP4MI_DEC(8, 8); break;
-    case 128: FP4MI_DEC(8, 16); break;
-    case 256: FP4MI_DEC(8, 32); break;
+    case 16: launch_decode_rows<BF16OUT, 16>(pk, s1, s2, n, y, st); break;
+    case 32: launch_decode_rows<BF16OUT, 32>(pk, s1, s2, n, y, st); break;
+    case 64: launch_decode_rows<BF16OUT, 64>(pk, s1, s2, n, y, st); break;
+    case 128: launch_decode_rows<BF16OUT, 128>(pk, s1, s2, n, y, st); break;
+    case 256: launch_decode_rows<BF16OUT, 256>(pk, s1, s2, n, y, st); break;
     case 512: FP4MI_DEC(8, 64); break;
     case 1024: FP4MI_DEC(16, 64); break;
   }
