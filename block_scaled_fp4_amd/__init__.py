@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libfp4mi.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with "
-                      "`python -m block_scaled_fp4_amd.build` (hipcc, gfx950)")
+                      "`python __graft_entry__.py` or `python block_scaled_fp4_amd/build.py` (hipcc, gfx950)")
 
 _lib = ctypes.CDLL(LIB_PATH)
 

@@ -1,6 +1,6 @@
 """Build libfp4mi.so (all HIP sources for gfx950) in-tree.
 
-Usage: python -m block_scaled_fp4_amd.build   (or call build()).
+Usage: python block_scaled_fp4_amd/build.py   (or call build()).
 """
 import os
 import shutil
