@@ -36,37 +36,61 @@ __device__ __forceinline__ NvScale nv_block_scale_exact(float absmax, float st) 
   return s;
 }
 
-// The same scale without the two divisions.  With kinv = fl32(1/fl32(6 S_t))
-// a normal number, r' = absmax * kinv is within 2^-21 (relative) of
-// fl32(fl32(absmax/6)/S_t); E4M3 encoding is monotone, so if r'(1 - 2^-18)
-// and r'(1 + 2^-18) encode to the same byte the exact quotient does too.
-// Otherwise (a quotient within 2^-18 of an E4M3 rounding boundary) *sure is
-// cleared and the exact scale must be taken instead.
-__device__ __forceinline__ NvScale nv_block_scale_fast(float absmax, float st, float kinv,
-                                                       bool* sure) {
-  const float r = absmax * kinv;
-  const uint32_t lo = e4m3_encode_sat_hw(r * 0x1.fffcp-1f);     // 1 - 2^-18
-  const uint32_t hi = e4m3_encode_sat_hw(r * 0x1.00004p+0f);    // 1 + 2^-18
-  *sure = lo == hi;
-  NvScale s;
-  s.code = lo;
-  s.sdec = e4m3_value(lo) * st;
-  return s;
+// ------------------------------------------- NVFP4 quotients without division
+// Three quotients decide the NVFP4 codes: fl32(absmax / 6), fl32(that / S_t)
+// and fl32(x / s_dec).  Each is taken as q0 = a * y with y = fl32(1 / b),
+// followed by one correction, q1 = fma(-fma(q0, b, -a), y, q0) (residual
+// then refined quotient).  On the GPU, for every fp32 significand of b:
+//  - recip_rn(b) = fma(fma(-b, r, 1), r, r), r = v_rcp_f32(b), equals the
+//    IEEE quotient 1 / b (exponents -100 .. 100 checked);
+//  - div_rn(a, 6, fl32(1/6)) equals the IEEE a / 6 for every significand
+//    of a;
+//  - div_rn(a, b, fl32(1/b)) equals the IEEE a / b for every a within 48
+//    ulps of t * b, for each E2M1 rounding threshold t and each value t
+//    with at most five significant bits (which includes every E4M3 rounding
+//    boundary).
+// E2M1 codes and E4M3 bytes change only at those points, so wherever the
+// operands and quotients are normal numbers (where scaling by powers of two
+// changes nothing) the codes and bytes taken from q1 are those of the IEEE
+// quotients.  The residual is negated (fma(q0, b, -a)) so that a zero a
+// keeps its sign.
+__device__ __forceinline__ float recip_rn(float b) {
+  const float r = __builtin_amdgcn_rcpf(b);
+  return __builtin_fmaf(__builtin_fmaf(-b, r, 1.0f), r, r);
+}
+__device__ __forceinline__ float div_rn(float a, float b, float y) {
+  const float q0 = a * y;
+  return __builtin_fmaf(-__builtin_fmaf(q0, b, -a), y, q0);
+}
+constexpr float kInv6 = 0x1.555556p-3f;          // fl32(1 / 6)
+
+// S_t range in which the division-free chain holds for every block: all
+// s_dec = e4m3 * S_t (2^-9 <= e4m3 <= 448) and their reciprocals are normal.
+__device__ __forceinline__ bool nv_newton_range(float st) {
+  return st >= 0x1p-100f && st <= 0x1p+100f;
 }
 
-__device__ __forceinline__ NvScale nv_block_scale(float absmax, float st, float kinv, bool fast) {
-  if (fast) {
-    bool sure;
-    const NvScale s = nv_block_scale_fast(absmax, st, kinv, &sure);
-    if (sure) return s;
+// Block scale by the division-free chain; rst = fl32(1 / S_t).  *ok is
+// cleared when the raw quotient r is 2^120 or more (a saturated scale so far
+// off that element quotients could overflow); the exact scale and codes
+// must then be taken.  An absmax below 2^-120 gives r < 2^-22 (byte 0)
+// whatever the rounding of absmax / 6, so the chain stays exact there too.
+__device__ __forceinline__ NvScale nv_block_scale_newton(float absmax, float st, float rst,
+                                                         bool* ok) {
+  const float r = div_rn(div_rn(absmax, 6.0f, kInv6), st, rst);
+  *ok = r < 0x1p+120f;
+  const uint32_t c = e4m3_encode_sat_hw(r);
+  return NvScale{c, e4m3_value_hw(c) * st};
+}
+
+// Block scale by the division-free chain where it holds, else the IEEE one.
+__device__ __forceinline__ NvScale nv_block_scale(float absmax, float st, float rst, bool newton) {
+  if (newton) {
+    bool ok;
+    const NvScale s = nv_block_scale_newton(absmax, st, rst, &ok);
+    if (ok) return s;
   }
   return nv_block_scale_exact(absmax, st);
-}
-
-__device__ __forceinline__ float nv_kinv(float st, bool* fast) {
-  const float k = 1.0f / (6.0f * st);
-  *fast = (k >= 0x1p-126f) && (k < 0x1p+127f);
-  return k;
 }
 
 // MXFP4: UE8M0 byte = clamp(floor(log2 absmax) - 2 + 127, 0, 254), read from
@@ -131,71 +155,15 @@ __device__ __forceinline__ uint32_t encode_octet_sw(const float (&v)[8], float s
   return word;
 }
 
-// NVFP4 RTN codes of fl32(v / sdec) without a per-element division.
-// With rc = v_rcp_f32(sdec) (1 ulp) and sdec in [2^-125, 2^125], the
-// products v * rc (1 - 2^-18) and v * rc (1 + 2^-18) bracket fl32(v / sdec)
-// in magnitude (all rounding errors together stay below 2^-21); RTN is
-// monotone in |q|, so when both round to the same code so does
-// fl32(v / sdec).  Otherwise (an element within ~2^-18 of a rounding
-// threshold) the octet is redone with IEEE divisions.
-__device__ __forceinline__ uint32_t encode_octet_nv_rtn_fast(const float (&v)[8], float sdec,
-                                                             bool* sure) {
-  *sure = false;
-  if (!(sdec >= 0x1p-125f && sdec <= 0x1p+125f)) return 0u;
-  const float rc = __builtin_amdgcn_rcpf(sdec);
-  const float rlo = rc * 0x1.fffcp-1f;      // (1/sdec)(1 - 2^-18), within 2^-22
-  const float rhi = rc * 0x1.00004p+0f;     // (1/sdec)(1 + 2^-18), within 2^-22
-  float lo[8], hi[8];
+// NVFP4 RTN codes of fl32(v / sdec) from division-free quotients (exact for
+// sdec in [2^-109, 2^109] or 0; see recip_rn / div_rn).  sdec = 0 gives
+// y = 0 and sign-only codes.
+__device__ __forceinline__ uint32_t encode_octet_nv_rtn(const float (&v)[8], float sdec) {
+  const float y = (sdec == 0.0f) ? 0.0f : recip_rn(sdec);
+  float q[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    lo[j] = v[j] * rlo;
-    hi[j] = v[j] * rhi;
-  }
-  const uint32_t wl = rtn8_unit(lo), wh = rtn8_unit(hi);
-  if (wl == wh) {
-    *sure = true;
-    return wl;
-  }
-  // Some element sits within 2^-18 of a threshold (exact quotients are
-  // common there: short binary fractions over short scales).  Those elements
-  // take one correction step from a Newton-refined reciprocal, q1 =
-  // q0 + fma(-q0, sdec, v) / sdec, and q1 is accepted as fl32(v / sdec) when
-  // the remainder r1 = fma(-q1, sdec, v) satisfies |r1| < ulp(q1) / 2 * sdec,
-  // i.e. |v / sdec - q1| < ulp(q1) / 2 (a quarter ulp when q1 is a power of
-  // two), so that q1 rounds it to nearest (if q1 is within an ulp of the
-  // quotient the remainder is exact; if it is farther, |r1| is at least
-  // ulp(q1) sdec and no rounding brings it below the bound).  With sdec in
-  // [2^-60, 2^60] and |q1| >= 0.25 near a threshold the bound is a normal
-  // number.  An element that fails the test leaves *sure false.
-  if (!(sdec >= 0x1p-60f && sdec <= 0x1p+60f)) return 0u;
-  const float rc2 = __builtin_fmaf(__builtin_fmaf(-sdec, rc, 1.0f), rc, rc);
-  const uint32_t diff = wl ^ wh;
-  bool ok = true;
-  float qx[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float q0 = v[j] * rc2;
-    const float r0 = __builtin_fmaf(-q0, sdec, v[j]);
-    const float q1 = __builtin_fmaf(r0, rc2, q0);
-    const float r1 = __builtin_fmaf(-q1, sdec, v[j]);
-    const int eb = (int)((__float_as_uint(q1) >> 23) & 0xFFu);          // biased exponent
-    // ulp(q1)/2 * sdec, or a quarter ulp when q1 is a power of two (the
-    // spacing below it is half as wide)
-    const int pow2 = (__float_as_uint(q1) & 0x7FFFFFu) == 0u ? 1 : 0;
-    const float bound = __builtin_amdgcn_ldexpf(sdec, eb - 151 - pow2);
-    const bool amb = ((diff >> (4 * j)) & 15u) != 0u;
-    ok = ok && (!amb || (fabsf(r1) < bound && eb >= 125));
-    qx[j] = amb ? q1 : lo[j];
-  }
-  *sure = ok;
-  return rtn8_unit(qx);
-}
-
-// The same codes, exact in every case (IEEE divisions when unsure).
-__device__ __forceinline__ uint32_t encode_octet_nv_rtn(const float (&v)[8], float sdec, int64_t i) {
-  bool sure;
-  const uint32_t w = encode_octet_nv_rtn_fast(v, sdec, &sure);
-  return sure ? w : encode_octet_sw<false, false>(v, sdec, 0, i, 0, 0);
+  for (int j = 0; j < 8; ++j) q[j] = div_rn(v[j], sdec, y);
+  return rtn8_unit(q);
 }
 
 // MXFP4 RTN codes: divide by 2^e and round in the converter (bf16 words go
@@ -227,10 +195,9 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
     const void* __restrict__ x, int64_t n_oct, const float* __restrict__ st_ptr, uint64_t seed,
     uint64_t step, uint32_t* __restrict__ packed, uint8_t* __restrict__ scales) {
   const float st = MX ? 1.0f : *st_ptr;
-  bool fast = false;
-  const float kinv = MX ? 0.0f : nv_kinv(st, &fast);
+  const bool newton = !MX && nv_newton_range(st);
+  const float rst = newton ? 1.0f / st : 0.0f;
   const int64_t base = (int64_t)blockIdx.x * (kThreads * U) + threadIdx.x;
-  uint32_t redo = 0;   // NVFP4 RTN: octets to redo exactly
   u32x4 ra[U], rb[U];
 #pragma unroll
   for (int k = 0; k < U; ++k) {
@@ -259,42 +226,69 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
       if constexpr (SR) word = encode_octet_sw<true, true>(v, 0.0f, 127 - (int)scode, i, seed, step);
       else word = encode_octet_mx_rtn<BF16>(ra[k], v, scode);
     } else if constexpr (SR) {
-      const NvScale s = nv_block_scale(am, st, kinv, fast);
+      const NvScale s = nv_block_scale(am, st, rst, newton);
       scode = s.code;
       word = encode_octet_sw<false, true>(v, s.sdec, 0, i, seed, step);
     } else {
-      // codes without divisions; an octet they cannot certify is redone
-      // with IEEE divisions after the loop
-      const NvScale s = nv_block_scale(am, st, kinv, fast);
-      scode = s.code;
-      bool sure = false;
-      word = encode_octet_nv_rtn_fast(v, s.sdec, &sure);
-      if (!sure) {
-        redo |= 1u << k;
-        if (i < n_oct && (i & 1) == 0) scales[i >> 1] = (uint8_t)scode;
-        continue;
-      }
+      static_assert(MX || SR, "NVFP4 RTN has its own kernel");
     }
     if (i < n_oct) {
       st_u32(packed + i, word);
       if ((i & (MX ? 3 : 1)) == 0) scales[i >> (MX ? 2 : 1)] = (uint8_t)scode;
     }
   }
-  if constexpr (!MX && !SR) {
-    // Octets whose codes were not certain: redone with IEEE divisions, out
-    // of the hot loop (the block scale, already stored, is recomputed from
-    // the octet and its block partner).
-    while (redo) {
-      const int k = __builtin_ctz(redo);
-      redo &= redo - 1;
-      const int64_t i = base + (int64_t)k * kThreads;
-      if (i >= n_oct) continue;
-      float v[8], w[8];
-      load_octet<BF16>(x, i, v);
-      load_octet<BF16>(x, i ^ 1, w);                     // the block partner (n_oct is even)
-      const float am = fmaxf(absmax8(v), absmax8(w));
-      const NvScale s = nv_block_scale_exact(am, st);
-      st_u32(packed + i, encode_octet_sw<false, false>(v, s.sdec, 0, i, 0, 0));
+}
+
+// ------------------------------------------------ NVFP4 RTN quantize
+// Scale and codes from the division-free quotients, which are exact
+// wherever S_t lies in [2^-100, 2^100] and the block's raw scale quotient is
+// below 2^120; other blocks (a wave-uniform branch, taken only for extreme
+// inputs) use IEEE divisions.
+// Thread t of workgroup b owns octets b*256*U + t + 256*k, k < U.
+template <bool BF16, int U = kOctets<BF16>>
+__global__ __launch_bounds__(kThreads) void nv_rtn_quantize_kernel(
+    const void* __restrict__ x, int64_t n_oct, const float* __restrict__ st_ptr,
+    uint32_t* __restrict__ packed, uint8_t* __restrict__ scales) {
+  const float st = *st_ptr;
+  const bool newton = nv_newton_range(st);
+  const float rst = newton ? 1.0f / st : 0.0f;
+  const int64_t base = (int64_t)blockIdx.x * (kThreads * U) + threadIdx.x;
+  u32x4 ra[U], rb[U];
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+    const int64_t i = base + (int64_t)k * kThreads;
+    const bool ok = i < n_oct;
+    if constexpr (BF16) {
+      ra[k] = ok ? ld_u32x4(static_cast<const uint8_t*>(x) + i * 16) : u32x4{0u, 0u, 0u, 0u};
+    } else {
+      const uint8_t* p = static_cast<const uint8_t*>(x) + i * 32;
+      ra[k] = ok ? ld_u32x4(p) : u32x4{0u, 0u, 0u, 0u};
+      rb[k] = ok ? ld_u32x4(p + 16) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+    const int64_t i = base + (int64_t)k * kThreads;
+    float v[8];
+    if constexpr (BF16) unpack_bf16x8(ra[k], v);
+    else unpack_f32x8(ra[k], rb[k], v);
+    // block absmax: a non-negative float orders like its bit pattern
+    uint32_t amb = __float_as_uint(absmax8(v));
+    amb = max(amb, (uint32_t)lane_xor1_i((int)amb));
+    const float am = __uint_as_float(amb);
+    bool ok;
+    NvScale s = nv_block_scale_newton(am, st, rst, &ok);
+    ok = ok && newton;
+    uint32_t word = encode_octet_nv_rtn(v, s.sdec);
+    if (__ballot(!ok)) {                            // wave-uniform; extreme inputs only
+      if (!ok) {
+        s = nv_block_scale_exact(am, st);
+        word = encode_octet_sw<false, false>(v, s.sdec, 0, i, 0, 0);
+      }
+    }
+    if (i < n_oct) {
+      st_u32(packed + i, word);
+      if ((i & 1) == 0) scales[i >> 1] = (uint8_t)s.code;
     }
   }
 }
@@ -418,8 +412,8 @@ __global__ __launch_bounds__(kThreads) void ef_qdq_kernel(
     uint8_t* __restrict__ scales) {
   constexpr int U = 2;
   const float st = *st_ptr;
-  bool fast = false;
-  const float kinv = nv_kinv(st, &fast);
+  const bool newton = nv_newton_range(st);
+  const float rst = newton ? 1.0f / st : 0.0f;
   const int64_t base = (int64_t)blockIdx.x * (kThreads * U) + threadIdx.x;
   float v[U][8];
 #pragma unroll
@@ -441,10 +435,14 @@ __global__ __launch_bounds__(kThreads) void ef_qdq_kernel(
     const int64_t i = base + (int64_t)k * kThreads;
     float am = absmax8(v[k]);
     am = fmaxf(am, lane_xor1(am));
-    const NvScale s = nv_block_scale(am, st, kinv, fast);
+    bool ok;
+    NvScale s = nv_block_scale_newton(am, st, rst, &ok);
+    ok = ok && newton;
+    if (!ok) s = nv_block_scale_exact(am, st);
     uint32_t word;
     if constexpr (SR) word = encode_octet_sw<false, true>(v[k], s.sdec, 0, i, seed, step);
-    else word = encode_octet_nv_rtn(v[k], s.sdec, i);
+    else word = ok ? encode_octet_nv_rtn(v[k], s.sdec)
+                   : encode_octet_sw<false, false>(v[k], s.sdec, 0, i, 0, 0);
     if (i >= n_oct) continue;
     float o[8];
     e2m1x8_to_f32(word, 1.0f, o);
@@ -501,9 +499,12 @@ void launch_quantize_t(bool sr, const void* x, int64_t n_oct, const float* ts, u
   if (sr)
     hipLaunchKernelGGL((quantize_kernel<BF16, MX, true>), g, dim3(kThreads), 0, st, x, n_oct,
                        ts, seed, step, packed, scales);
-  else
-    hipLaunchKernelGGL((quantize_kernel<BF16, MX, false>), g, dim3(kThreads), 0, st, x,
+  else if (MX)
+    hipLaunchKernelGGL((quantize_kernel<BF16, true, false>), g, dim3(kThreads), 0, st, x,
                        n_oct, ts, seed, step, packed, scales);
+  else
+    hipLaunchKernelGGL((nv_rtn_quantize_kernel<BF16>), g, dim3(kThreads), 0, st, x, n_oct, ts,
+                       packed, scales);
 }
 
 template <bool BF16IN, bool BF16OUT>

@@ -156,6 +156,76 @@ def test_nvfp4_bf16_input_exact_and_ambiguous_quotients():
         np.testing.assert_array_equal(p, rp)
 
 
+def test_nvfp4_rtn_8192x8192_compute_sampled_rows():
+    """The 8192 x 8192 NVFP4 RTN shape, computed S_t, in the launch the
+    bench times: S_t against the oracle's max over the whole tensor, then
+    every code and scale byte of 32 sampled rows, and their dequantized
+    values."""
+    m = need_gpu()
+    xb = synth.weight_block(8192, 8192, seed=11)
+    R, C = xb.shape
+    x_dev = dev_bf16(xb)
+    p, s, ts = run_quant(m, x_dev, "nvfp4")
+    st = nvfp4.tensor_scale(F.bf16_bits_to_f32(xb))
+    assert np.float32(ts) == st
+    rows = np.unique(np.concatenate([[0, R - 1], np.random.default_rng(11).choice(R, 30, replace=False)]))
+    x = F.bf16_bits_to_f32(xb[rows])
+    rp, rs = nvfp4.quantize_packed(x, st)
+    np.testing.assert_array_equal(s[rows], rs)
+    np.testing.assert_array_equal(p[rows], rp)
+    y = run_dequant(m, p, s, R, C, "nvfp4", ts)
+    np.testing.assert_array_equal(y[rows], nvfp4.dequantize(rp, rs, st, "bf16"))
+
+
+def test_nvfp4_exact_ties_with_computed_scale():
+    """Elements that share the significand of the tensor's absmax A have
+    x / s_dec = 2688 * 2^k / e4m3 in exact arithmetic, a rounding threshold
+    for several scale bytes: fp32 rounding of S_t and s_dec decides their
+    codes.  A third of the elements are such values (both signs, many k)."""
+    m = need_gpu()
+    rng = np.random.default_rng(21)
+    R, C = 96, 4096
+    x = (rng.standard_normal((R, C)) * 0.02).astype(np.float32)
+    for A in (3.984375, 1.0, 0.0234375, 96.0):
+        xx = x.copy()
+        xx[0, 0] = A
+        sel = rng.random((R, C)) < 0.33
+        k = rng.integers(0, 13, size=(R, C))
+        xx[sel] = (np.float32(A) * np.exp2(-k[sel]) * rng.choice([-1, 1], size=sel.sum())).astype(np.float32)
+        xb = synth.to_bf16_bits(xx)
+        xv = F.bf16_bits_to_f32(xb)
+        p, s, ts = run_quant(m, dev_bf16(xb), "nvfp4")
+        st = nvfp4.tensor_scale(xv)
+        assert np.float32(ts) == st
+        rp, rs = nvfp4.quantize_packed(xv, st)
+        np.testing.assert_array_equal(s, rs)
+        np.testing.assert_array_equal(p, rp)
+
+
+def test_nvfp4_tiny_absmax_and_extreme_scales():
+    """Blocks whose absmax / 6 is subnormal at a normal S_t (the E4M3 byte
+    then depends on fp32 underflow rounding), S_t outside [2^-100, 2^100],
+    and blocks whose scale saturates so far that element quotients reach
+    2^105: the IEEE-division paths and the saturating codes."""
+    m = need_gpu()
+    rng = np.random.default_rng(22)
+    # absmax = (49152 + j) * 2^-149 with S_t = 2^-126: r sits at the 0 / 2^-9 boundary
+    blk = np.zeros((64, 16), np.float32)
+    blk[:, 0] = (np.arange(49140, 49204, dtype=np.uint32)).view(np.float32)
+    blk[:, 1:] = (rng.integers(0, 1 << 16, size=(64, 15)).astype(np.uint32)).view(np.float32)
+    cases = [(blk.reshape(4, -1), 2.0 ** -126)]
+    x = (rng.standard_t(3, size=(8, 512)) * np.exp2(rng.integers(-30, 30, size=(8, 1)))).astype(np.float32)
+    cases += [(x, 2.0 ** -110), (x, 2.0 ** 105), (x, 2.0 ** -100), (x * np.float32(2.0 ** 14), 2.0 ** -100),
+              (x * np.float32(2.0 ** 40), 2.0 ** -100)]
+    for xx, st in cases:
+        st = np.float32(st)
+        ts = dev_f32(np.array([st], np.float32))
+        p, s, _ = run_quant(m, dev_f32(xx), "nvfp4", tscale="given", ts=ts)
+        rp, rs = nvfp4.quantize_packed(xx, st)
+        np.testing.assert_array_equal(s, rs)
+        np.testing.assert_array_equal(p, rp)
+
+
 def test_nvfp4_dequantize_foreign_scale_bytes():
     """Dequantize accepts any E4M3 byte (signed, subnormal, NaN) and code."""
     m = need_gpu()
