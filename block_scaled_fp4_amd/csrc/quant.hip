@@ -357,43 +357,74 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(
 // --------------------------------------------------- tensor amax (NVFP4)
 __global__ void zero_u32_kernel(uint32_t* p) { *p = 0u; }
 
-// max |x (+ r)| over the tensor into *out_bits: each workgroup reduces its
-// share (waves by DPP/shuffle, then LDS) and issues one atomic max on the
-// bit pattern of a non-negative float, which orders like the value.
+// max |x (+ r)| over the tensor into *out_bits.  The maximum of
+// non-negative floats is taken on their bit patterns (which order like the
+// values; bf16 magnitudes as 16-bit patterns).  Every atomic max on the one
+// word is serialised at the memory side (several ns each), so the grid is
+// kept to at most kAmaxGrid large workgroups, each with U octets per thread
+// in flight, and each workgroup issues a single atomic.
+constexpr int kAmaxThreads = 1024;
+constexpr int kAmaxGrid = 256;
+
 template <bool BF16, bool RES>
-__global__ __launch_bounds__(kThreads) void amax_kernel(const void* __restrict__ x,
-                                                        const float* __restrict__ r, int64_t n_oct,
-                                                        uint32_t* __restrict__ out_bits) {
-  constexpr int U = 2;
-  __shared__ float part[kThreads / 64];
-  float m = 0.0f;
-  const int64_t stride = (int64_t)gridDim.x * kThreads * U;
-  for (int64_t base = (int64_t)blockIdx.x * kThreads * U + threadIdx.x; base < n_oct; base += stride) {
-    float v[U][8];
+__global__ __launch_bounds__(kAmaxThreads) void amax_kernel(const void* __restrict__ x,
+                                                            const float* __restrict__ r,
+                                                            int64_t n_oct,
+                                                            uint32_t* __restrict__ out_bits) {
+  constexpr int U = (BF16 && !RES) ? 4 : 2;
+  __shared__ uint32_t part[kAmaxThreads / 64];
+  uint32_t m = 0;
+  const int64_t stride = (int64_t)gridDim.x * kAmaxThreads * U;
+  for (int64_t base = (int64_t)blockIdx.x * kAmaxThreads * U + threadIdx.x; base < n_oct;
+       base += stride) {
+    u32x4 a[U], b[U], c[U], d[U];
 #pragma unroll
     for (int k = 0; k < U; ++k) {
-      const int64_t i = base + (int64_t)k * kThreads;
-      if (i < n_oct) load8<BF16>(x, i, v[k]);
-      else for (int j = 0; j < 8; ++j) v[k][j] = 0.0f;
+      const int64_t i = base + (int64_t)k * kAmaxThreads;
+      const bool ok = i < n_oct;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      if constexpr (BF16) {
+        a[k] = ok ? ld_u32x4(static_cast<const uint8_t*>(x) + i * 16) : z;
+      } else {
+        a[k] = ok ? ld_u32x4(static_cast<const uint8_t*>(x) + i * 32) : z;
+        b[k] = ok ? ld_u32x4(static_cast<const uint8_t*>(x) + i * 32 + 16) : z;
+      }
       if constexpr (RES) {
-        float rr[8];
-        if (i < n_oct) load8<false>(r, i, rr);
-        else for (int j = 0; j < 8; ++j) rr[j] = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[k][j] = v[k][j] + rr[j];
+        c[k] = ok ? ld_u32x4(reinterpret_cast<const uint8_t*>(r) + i * 32) : z;
+        d[k] = ok ? ld_u32x4(reinterpret_cast<const uint8_t*>(r) + i * 32 + 16) : z;
       }
     }
 #pragma unroll
-    for (int k = 0; k < U; ++k) m = fmaxf(m, absmax8(v[k]));
+    for (int k = 0; k < U; ++k) {
+      if constexpr (BF16 && !RES) {
+        const uint32_t w0 = a[k].x & 0x7FFF7FFFu, w1 = a[k].y & 0x7FFF7FFFu;
+        const uint32_t w2 = a[k].z & 0x7FFF7FFFu, w3 = a[k].w & 0x7FFF7FFFu;
+        const uint32_t hi = max(max(w0 >> 16, w1 >> 16), max(w2 >> 16, w3 >> 16));
+        const uint32_t lo = max(max(w0 & 0xFFFFu, w1 & 0xFFFFu), max(w2 & 0xFFFFu, w3 & 0xFFFFu));
+        m = max(m, max(hi, lo) << 16);
+      } else {
+        float v[8];
+        if constexpr (BF16) unpack_bf16x8(a[k], v);
+        else unpack_f32x8(a[k], b[k], v);
+        if constexpr (RES) {
+          float rr[8];
+          unpack_f32x8(c[k], d[k], rr);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] = v[j] + rr[j];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) m = max(m, __float_as_uint(v[j]) & 0x7FFFFFFFu);
+      }
+    }
   }
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
-    float b = part[0];
-    for (int w = 1; w < kThreads / 64; ++w) b = fmaxf(b, part[w]);
-    atomicMax(out_bits, __float_as_uint(b));
+    uint32_t q = part[0];
+    for (int w = 1; w < kAmaxThreads / 64; ++w) q = max(q, part[w]);
+    atomicMax(out_bits, q);
   }
 }
 
@@ -478,15 +509,17 @@ __global__ __launch_bounds__(kThreads) void ef_qdq_kernel(
 int launch_tensor_scale(const void* x, bool bf16, const float* res, int64_t n_oct, float* ts,
                         hipStream_t st) {
   hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(1), 0, st, reinterpret_cast<uint32_t*>(ts));
-  int64_t g = blocks_for(n_oct, 2);
-  if (g > 1024) g = 1024;
+  const int u = (bf16 && !res) ? 4 : 2;
+  int64_t g = (n_oct + (int64_t)kAmaxThreads * u - 1) / ((int64_t)kAmaxThreads * u);
+  if (g > kAmaxGrid) g = kAmaxGrid;
+  const dim3 grid((unsigned)g), blk(kAmaxThreads);
   uint32_t* bits = reinterpret_cast<uint32_t*>(ts);
   if (bf16) {
-    if (res) hipLaunchKernelGGL((amax_kernel<true, true>), dim3((unsigned)g), dim3(kThreads), 0, st, x, res, n_oct, bits);
-    else     hipLaunchKernelGGL((amax_kernel<true, false>), dim3((unsigned)g), dim3(kThreads), 0, st, x, res, n_oct, bits);
+    if (res) hipLaunchKernelGGL((amax_kernel<true, true>), grid, blk, 0, st, x, res, n_oct, bits);
+    else     hipLaunchKernelGGL((amax_kernel<true, false>), grid, blk, 0, st, x, res, n_oct, bits);
   } else {
-    if (res) hipLaunchKernelGGL((amax_kernel<false, true>), dim3((unsigned)g), dim3(kThreads), 0, st, x, res, n_oct, bits);
-    else     hipLaunchKernelGGL((amax_kernel<false, false>), dim3((unsigned)g), dim3(kThreads), 0, st, x, res, n_oct, bits);
+    if (res) hipLaunchKernelGGL((amax_kernel<false, true>), grid, blk, 0, st, x, res, n_oct, bits);
+    else     hipLaunchKernelGGL((amax_kernel<false, false>), grid, blk, 0, st, x, res, n_oct, bits);
   }
   hipLaunchKernelGGL(tensor_scale_finalize_kernel, dim3(1), dim3(1), 0, st, ts);
   return launch_status();
