@@ -146,11 +146,14 @@ def headline(args, torch, fp4, np, synth):
     q_ms, _ = graph_time(torch, quant, reps, replays)
     d_ms, _ = graph_time(torch, dequant, reps, replays)
     check()
+    # achievable-bandwidth reference: a plain device copy of the bf16 input
+    # (read 2n + write 2n bytes) over the same rotating buffer sets
+    c_ms, _ = graph_time(torch, lambda k: sets[k % nsets]["y"].copy_(sets[k % nsets]["x"]), reps, replays)
     steps = reps * replays
     log(f"[bench] {mode}: step {ms_step * 1e3:.2f} us; quantize {q_ms * 1e3:.2f} us; "
         f"dequantize {d_ms * 1e3:.2f} us ({steps} steps)")
     return dict(rows=rows, cols=cols, n=n, q_bytes=q_bytes, dq_bytes=dq_bytes, ms_step=ms_step,
-                q_ms=q_ms, d_ms=d_ms, nsets=nsets, footprint=foot, xb=xb, steps=steps, mode=mode)
+                q_ms=q_ms, d_ms=d_ms, copy_GBps=4 * n / (c_ms * 1e-3) / 1e9, nsets=nsets, footprint=foot, xb=xb, steps=steps, mode=mode)
 
 
 def copy_probe(args, torch):
@@ -462,6 +465,7 @@ def main():
         "kernels_us": {"quantize": round(h["q_ms"] * 1e3, 2), "dequantize": round(h["d_ms"] * 1e3, 2)},
         "timing": f"HIP graph of {args.graph_steps} steps replayed, HIP events on the launch stream ({h['mode']})",
         "roofline": roof,
+        "copy_reference_GBps": round(h["copy_GBps"], 1),
     }
     if not args.no_breakdown:
         res["breakdown"] = breakdown(args, torch, fp4, np, synth)

@@ -630,14 +630,16 @@ extern "C" int fp4_dequantize(const uint8_t* packed, const uint8_t* scales,
   hipStream_t st = as_stream(stream);
   const int64_t n_oct = n / 8;
   if (!grid_fits(n_oct)) return FP4_ESHAPE;
-  const dim3 g((unsigned)blocks_for(n_oct, 1));
+  // two octets per thread: two code loads in flight per lane
+  constexpr int U = 2;
+  const dim3 g((unsigned)blocks_for(n_oct, U));
   const uint32_t* pk = reinterpret_cast<const uint32_t*>(packed);
   if (out_dtype == FP4_DTYPE_BF16) {
-    if (mx) hipLaunchKernelGGL((dequantize_kernel<true, true>), dim3(g), dim3(kThreads), 0, st, pk, scales, tensor_scale, n_oct, y);
-    else    hipLaunchKernelGGL((dequantize_kernel<true, false>), dim3(g), dim3(kThreads), 0, st, pk, scales, tensor_scale, n_oct, y);
+    if (mx) hipLaunchKernelGGL((dequantize_kernel<true, true, U>), dim3(g), dim3(kThreads), 0, st, pk, scales, tensor_scale, n_oct, y);
+    else    hipLaunchKernelGGL((dequantize_kernel<true, false, U>), dim3(g), dim3(kThreads), 0, st, pk, scales, tensor_scale, n_oct, y);
   } else {
-    if (mx) hipLaunchKernelGGL((dequantize_kernel<false, true>), dim3(g), dim3(kThreads), 0, st, pk, scales, tensor_scale, n_oct, y);
-    else    hipLaunchKernelGGL((dequantize_kernel<false, false>), dim3(g), dim3(kThreads), 0, st, pk, scales, tensor_scale, n_oct, y);
+    if (mx) hipLaunchKernelGGL((dequantize_kernel<false, true, U>), dim3(g), dim3(kThreads), 0, st, pk, scales, tensor_scale, n_oct, y);
+    else    hipLaunchKernelGGL((dequantize_kernel<false, false, U>), dim3(g), dim3(kThreads), 0, st, pk, scales, tensor_scale, n_oct, y);
   }
   return launch_status();
 }
