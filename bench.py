@@ -271,6 +271,10 @@ def breakdown(args, torch, fp4, np, synth):
     nb = T * H // 2 + T * H // 32 + T * H + 4 * (T * H // 128)
     add("mxfp4_row_to_fp8_col", "65536x7168, 256 Zipf(1.1) experts", nb,
         timed(lambda k: fp4.mxfp4_row_to_fp8_col(pk, sc, offd, H, o8, s8), max(iters // 2, 5)))
+    # the same rows -> FP8 rows (no transpose): the dispatch receiver
+    o8r, s8r = o8.view(T, H), s8.view(T, H // 128)
+    add("mxfp4_row_to_fp8_row", "65536x7168", nb,
+        timed(lambda k: fp4.mxfp4_row_to_fp8_row(pk, sc, H, o8r, s8r), max(iters // 2, 5)))
     return out
 
 

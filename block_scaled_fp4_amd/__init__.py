@@ -9,7 +9,7 @@ import: there is no CPU fallback.
 
 Entry points (same names as the C ABI in include/fp4mi.h):
   fp4_quantize, fp4_dequantize, fp4quant_encode, fp4quant_decode,
-  fp4_errfeedback_qdq, mxfp4_row_to_fp8_col
+  fp4_errfeedback_qdq, mxfp4_row_to_fp8_col, mxfp4_row_to_fp8_row
 plus ErrorFeedback, a name-keyed holder of residual buffers in the style of
 the fp4-train page's ErrorFeedback.qdq(name, x, step).
 """
@@ -42,6 +42,7 @@ _SIGS = {
     "fp4quant_decode": [_p, _p, _p, _i64, _i64, _i32, _p, _i, _p],
     "fp4_errfeedback_qdq": [_p, _i, _i64, _i64, _p, _p, _i, _i, _u64, _u64, _i, _p, _p, _p, _p],
     "mxfp4_row_to_fp8_col": [_p, _p, _p, _i32, _i64, _i64, _p, _p, _p],
+    "mxfp4_row_to_fp8_row": [_p, _p, _i64, _i64, _p, _p, _p],
 }
 for _name, _args in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -199,6 +200,22 @@ def mxfp4_row_to_fp8_col(packed, scales_e8m0, token_offsets, hidden, fp8_out=Non
     _check("mxfp4_row_to_fp8_col", _lib.mxfp4_row_to_fp8_col(
         _ptr(packed), _ptr(scales_e8m0), _ptr(token_offsets), E, T, hidden, _ptr(fp8_out),
         _ptr(fp8_scales), _stream(stream)))
+    return fp8_out, fp8_scales
+
+
+def mxfp4_row_to_fp8_row(packed, scales_e8m0, hidden, fp8_out=None, fp8_scales=None,
+                         stream=None):
+    """MXFP4 rows [T, H/2] (+ UE8M0 [T, H/32]) -> FP8 E4M3 rows [T, H] and
+    fp32 block scales [T, H/128] (no transpose)."""
+    _dev(packed)
+    T = packed.shape[0]
+    if fp8_out is None:
+        fp8_out = torch.empty((T, hidden), dtype=torch.uint8, device=packed.device)
+    if fp8_scales is None:
+        fp8_scales = torch.empty((T, hidden // 128), dtype=torch.float32, device=packed.device)
+    _check("mxfp4_row_to_fp8_row", _lib.mxfp4_row_to_fp8_row(
+        _ptr(packed), _ptr(scales_e8m0), T, hidden, _ptr(fp8_out), _ptr(fp8_scales),
+        _stream(stream)))
     return fp8_out, fp8_scales
 
 

@@ -506,6 +506,62 @@ __global__ __launch_bounds__(kThreads) void fp8col_kernel(
   }
 }
 
+// ------------------------------------------------------------ FP8 rows
+// FP4RowToFP8Row: the same remap and 4-to-1 scale alignment with no
+// transpose.  Thread-item s is one 32-channel sub-block of one token: its 16
+// code bytes sit at 16 s, its block's four UE8M0 bytes are scale dword s / 4
+// (H / 32 is a multiple of 4), its 32 FP8 bytes go to 32 s and its block's
+// fp32 scale to element s / 4 -- every access a plain stream.
+constexpr int kRowItems = 2;                          // sub-blocks per thread
+
+__global__ __launch_bounds__(kThreads) void fp8row_kernel(const uint8_t* __restrict__ packed,
+                                                         const uint32_t* __restrict__ sb4,
+                                                         int64_t n_sub, uint8_t* __restrict__ out,
+                                                         float* __restrict__ sc_out) {
+  __shared__ uint32_t lut[(kMaxShift + 1) * 2];
+  if (threadIdx.x < (kMaxShift + 1) * 2) {
+    const int d = threadIdx.x >> 1, half = threadIdx.x & 1;
+    uint32_t w = 0;
+    for (int k = 0; k < 4; ++k) w |= remap_e2m1_to_e4m3((uint32_t)(4 * half + k), d) << (8 * k);
+    lut[threadIdx.x] = w;
+  }
+  const int64_t base = (int64_t)blockIdx.x * (kThreads * kRowItems) + threadIdx.x;
+  u32x4 cw[kRowItems];
+  uint32_t s4[kRowItems];
+#pragma unroll
+  for (int k = 0; k < kRowItems; ++k) {
+    const int64_t s = base + (int64_t)k * kThreads;
+    const bool ok = s < n_sub;
+    cw[k] = ok ? ld_u32x4(packed + 16 * s) : u32x4{0u, 0u, 0u, 0u};
+    s4[k] = ok ? sb4[s >> 2] : 0u;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kRowItems; ++k) {
+    const int64_t s = base + (int64_t)k * kThreads;
+    if (s >= n_sub) continue;
+    const uint32_t v4 = s4[k];
+    const uint32_t s_tgt = max(max(v4 & 0xFFu, (v4 >> 8) & 0xFFu), max((v4 >> 16) & 0xFFu, v4 >> 24));
+    const uint32_t s_sub = (v4 >> (8 * (s & 3))) & 0xFFu;
+    const int d = min((int)(s_tgt - s_sub), kMaxShift);
+    const uint32_t tlo = lut[2 * d], thi = lut[2 * d + 1];
+    const uint32_t ww[4] = {cw[k].x, cw[k].y, cw[k].z, cw[k].w};
+    uint32_t o[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      // byte i of ww[q]: channel 8q+2i (low nibble) and 8q+2i+1 (high)
+      const uint32_t w = ww[q];
+      const uint32_t me = __builtin_amdgcn_perm(thi, tlo, w & 0x07070707u) | ((w << 4) & 0x80808080u);
+      const uint32_t mo = __builtin_amdgcn_perm(thi, tlo, (w >> 4) & 0x07070707u) | (w & 0x80808080u);
+      o[2 * q] = __builtin_amdgcn_perm(mo, me, 0x05010400u);       // channels 8q .. 8q+3
+      o[2 * q + 1] = __builtin_amdgcn_perm(mo, me, 0x07030602u);   // channels 8q+4 .. 8q+7
+    }
+    st_u32x4(out + 32 * s, u32x4{o[0], o[1], o[2], o[3]});
+    st_u32x4(out + 32 * s + 16, u32x4{o[4], o[5], o[6], o[7]});
+    if ((s & 3) == 0) sc_out[s >> 2] = __builtin_amdgcn_ldexpf(1.0f, (int)s_tgt - 127);
+  }
+}
+
 }  // namespace
 }  // namespace fp4mi
 
@@ -544,5 +600,30 @@ extern "C" int mxfp4_row_to_fp8_col(const uint8_t* packed, const uint8_t* scales
   hipLaunchKernelGGL(fp8col_kernel, dim3((unsigned)grid), dim3(kThreads), 0, st, packed,
                      scales_e8m0, token_offsets, num_experts, total_tokens, hidden, nchunks,
                      per_xcd, fp8_out, fp8_scales);
+  return launch_status();
+}
+
+extern "C" int mxfp4_row_to_fp8_row(const uint8_t* packed, const uint8_t* scales_e8m0,
+                                    int64_t total_tokens, int64_t hidden, uint8_t* fp8_out,
+                                    float* fp8_scales, void* stream) {
+  if (total_tokens < 0 || hidden <= 0 || hidden % 128) return FP4_ESHAPE;
+  int64_t n;
+  if (!checked_count(total_tokens, hidden, &n)) return FP4_ESHAPE;
+  if (n == 0) return FP4_OK;
+  if (!packed || !scales_e8m0 || !fp8_out || !fp8_scales) return FP4_EINVAL;
+  if (!is_aligned(packed, 16) || !is_aligned(scales_e8m0, 4) || !is_aligned(fp8_out, 16) ||
+      !is_aligned(fp8_scales, 4))
+    return FP4_EALIGN;
+  const int64_t pb = n / 2, sbb = n / 32, ob = n, scb = (n / 128) * 4;
+  if (overlaps(fp8_out, ob, packed, pb) || overlaps(fp8_out, ob, scales_e8m0, sbb) ||
+      overlaps(fp8_scales, scb, packed, pb) || overlaps(fp8_scales, scb, scales_e8m0, sbb) ||
+      overlaps(fp8_out, ob, fp8_scales, scb))
+    return FP4_EOVERLAP;
+  const int64_t n_sub = n / 32;
+  const int64_t grid = (n_sub + kThreads * kRowItems - 1) / (kThreads * kRowItems);
+  if (grid > 0x7FFFFFFF) return FP4_ESHAPE;
+  hipLaunchKernelGGL(fp8row_kernel, dim3((unsigned)grid), dim3(kThreads), 0, as_stream(stream),
+                     packed, reinterpret_cast<const uint32_t*>(scales_e8m0), n_sub, fp8_out,
+                     fp8_scales);
   return launch_status();
 }

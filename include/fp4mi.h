@@ -194,6 +194,27 @@ int mxfp4_row_to_fp8_col(const uint8_t* packed, const uint8_t* scales_e8m0,
                          int64_t total_tokens, int64_t hidden,
                          uint8_t* fp8_out, float* fp8_scales, void* stream);
 
+/*
+ * mxfp4_row_to_fp8_row -- MXFP4 rows -> FP8 E4M3 rows, no transpose: the
+ * forward receiver that the MoE report names FP4RowToFP8Row beside
+ * FP4RowToFP8Col ("Practical FP4 Training for Large-Scale MoE Models on
+ * Hopper GPUs", section "核心技术贡献", items 1 and 2), with the same
+ * per-value exponent remap and 4-to-1 scale alignment:
+ *   S_tgt = max of the four UE8M0 bytes of a 128-channel block;
+ *   out[t, h] = E4M3_RNE_sat(e2m1(code[t,h]) * 2^-(S_tgt - S_sub));
+ *   fp8_scales[t, b] = 2^(S_tgt - 127) (fp32).
+ *
+ *  packed         [T, H/2] MXFP4 codes, 16-byte aligned
+ *  scales_e8m0    [T, H/32] UE8M0 bytes (0xFF outside the contract), 4-byte aligned
+ *  total_tokens   T >= 0;  hidden H > 0, H % 128 == 0
+ *  fp8_out        out [T, H] E4M3 bytes, 16-byte aligned
+ *  fp8_scales     out fp32 [T, H/128], 4-byte aligned
+ * Outputs must not overlap inputs or each other.
+ */
+int mxfp4_row_to_fp8_row(const uint8_t* packed, const uint8_t* scales_e8m0,
+                         int64_t total_tokens, int64_t hidden,
+                         uint8_t* fp8_out, float* fp8_scales, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* fp4_status_string(int status);
 

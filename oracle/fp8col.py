@@ -1,5 +1,5 @@
-"""MXFP4 rows -> FP8 E4M3 columns, per ragged expert shard (oracle; test
-infrastructure only).
+"""MXFP4 rows -> FP8 E4M3 columns, per ragged expert shard, and MXFP4 rows
+-> FP8 E4M3 rows (oracle; test infrastructure only).
 
 Follows the report on "Practical FP4 Training for Large-Scale MoE Models on
 Hopper GPUs": "核心技术贡献" item 1 (direct FP4-to-FP8 conversion: 32-element
@@ -52,3 +52,27 @@ def convert(packed, scale_bytes, offsets, H):
         sc = np.exp2(tgt.astype(np.float64) - 127.0).astype(np.float32)  # [n, H/128]
         sc_out[(H // 128) * a: (H // 128) * b] = sc.T.reshape(-1)
     return out, sc_out
+
+
+def convert_rows(packed, scale_bytes, H):
+    """MXFP4 rows -> FP8 E4M3 rows, no transpose: the receiver that the MoE
+    report names FP4RowToFP8Row beside FP4RowToFP8Col ("核心技术贡献" items
+    1-2), with the same value-level remap as convert():
+      S_tgt = max of the four UE8M0 bytes of each 128-channel block;
+      out[t, h] = e4m3_RNE_sat( e2m1(code[t, h]) * 2**-(S_tgt - S_sub) );
+      fp32 scale[t, b] = 2**(S_tgt - 127).
+    packed uint8 [T, H/2]; scale_bytes uint8 [T, H/32].
+    Returns (fp8 bytes uint8 [T, H], fp32 scales float32 [T, H/128])."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    sb = np.asarray(scale_bytes, dtype=np.uint8).astype(np.int64)
+    T = packed.shape[0]
+    assert H % 128 == 0 and packed.shape[1] * 2 == H and sb.shape == (T, H // 32)
+    if (sb == 0xFF).any():
+        raise ValueError("UE8M0 NaN scale is outside the contract")
+    codes = F.unpack_codes(packed)                               # [T, H]
+    tgt = sb.reshape(T, H // 128, 4).max(axis=2)                 # [T, H/128]
+    d = np.repeat(tgt, 4, axis=1) - sb                           # [T, H/32]
+    val = F.e2m1_decode(codes).reshape(T, H // 32, 32) * np.exp2(-d[..., None].astype(np.float64))
+    out = F.e4m3_encode(val.reshape(T, H))
+    sc = np.exp2(tgt.astype(np.float64) - 127.0).astype(np.float32)
+    return out.astype(np.uint8), sc

@@ -25,14 +25,15 @@ def header_constants():
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
-        pytest.fail("libfp4mi.so is not built (python -m block_scaled_fp4_amd.build)")
+        pytest.fail("libfp4mi.so is not built (python __graft_entry__.py)")
     return ctypes.CDLL(LIB)
 
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) >= {"fp4_quantize", "fp4_dequantize", "fp4quant_encode", "fp4quant_decode",
-                          "fp4_errfeedback_qdq", "mxfp4_row_to_fp8_col", "fp4_status_string",
+                          "fp4_errfeedback_qdq", "mxfp4_row_to_fp8_col", "mxfp4_row_to_fp8_row",
+                          "fp4_status_string",
                           "fp4_abi_version"}
     for n in names:
         assert hasattr(lib, n), n
@@ -122,3 +123,21 @@ def test_other_entry_points_validation(lib):
     dq.argtypes = [P, P, P, I64, I64, I, P, I, P]
     assert dq(A, A + (1 << 30), A + (2 << 30), 4, 64, 0, A + 32, 1, None) == c["FP4_EOVERLAP"]
     assert dq(A, A + (1 << 30), None, 4, 64, 0, A + (3 << 30), 1, None) == c["FP4_EINVAL"]
+
+
+def test_fp8_row_validation(lib):
+    c = header_constants()
+    f = lib.mxfp4_row_to_fp8_row
+    f.argtypes = [P, P, I64, I64, P, P, P]
+
+    def call(packed=A, sb=A + (1 << 30), T=4, H=256, out=A + (2 << 30), sc=A + (3 << 30)):
+        return f(packed, sb, T, H, out, sc, None)
+
+    assert call(H=200) == c["FP4_ESHAPE"]                      # H % 128
+    assert call(T=-1) == c["FP4_ESHAPE"]
+    assert call(T=0) == c["FP4_OK"]                            # empty: no-op
+    assert call(packed=None) == c["FP4_EINVAL"]
+    assert call(out=A + (2 << 30) + 4) == c["FP4_EALIGN"]      # FP8 rows need 16-byte alignment
+    assert call(sb=A + (1 << 30) + 2) == c["FP4_EALIGN"]
+    assert call(out=A + 16) == c["FP4_EOVERLAP"]               # output inside the codes
+    assert call(sc=A + (2 << 30) + 64) == c["FP4_EOVERLAP"]    # scales inside the FP8 rows

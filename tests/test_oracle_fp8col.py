@@ -1,5 +1,5 @@
-"""Pins of the MXFP4-row -> FP8-column converter (MoE report, "核心技术贡献"
-items 1-3) -- CPU only."""
+"""Pins of the MXFP4-row -> FP8-column and -> FP8-row converters (MoE
+report, "核心技术贡献" items 1-3) -- CPU only."""
 import numpy as np
 import torch
 
@@ -66,3 +66,38 @@ def test_stepwise_equivalence_on_quantized_activations():
         ref = torch.from_numpy((deq[a:b] / scale).astype(np.float32)).to(torch.float8_e4m3fn)
         ref = ref.view(torch.uint8).numpy().T.reshape(-1)
         np.testing.assert_array_equal(out[384 * a: 384 * b], ref)
+
+
+def test_rows_are_the_columns_untransposed():
+    """The row converter and the (separately pinned) column converter give
+    the same FP8 bytes and scales, one per-expert transpose apart."""
+    rng = np.random.default_rng(4)
+    H = 384
+    counts = np.array([7, 0, 1, 30, 2])
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    T = int(off[-1])
+    packed = rng.integers(0, 256, size=(T, H // 2), dtype=np.uint8)
+    sb = rng.integers(100, 140, size=(T, H // 32), dtype=np.uint8)
+    ro, rs = fp8col.convert_rows(packed, sb, H)
+    co, cs = fp8col.convert(packed, sb, off, H)
+    assert ro.shape == (T, H) and rs.shape == (T, H // 128)
+    for e in range(counts.size):
+        a, n = int(off[e]), int(counts[e])
+        np.testing.assert_array_equal(co[H * a: H * (a + n)].reshape(H, n), ro[a:a + n].T)
+        np.testing.assert_array_equal(cs[(H // 128) * a: (H // 128) * (a + n)].reshape(H // 128, n),
+                                      rs[a:a + n].T)
+
+
+def test_rows_lossless_when_shift_at_most_8():
+    """value * scale is unchanged for every element whose shift d <= 8."""
+    rng = np.random.default_rng(5)
+    T, H = 6, 256
+    packed = rng.integers(0, 256, size=(T, H // 2), dtype=np.uint8)
+    sb = rng.integers(120, 129, size=(T, H // 32), dtype=np.uint8)
+    out, sc = fp8col.convert_rows(packed, sb, H)
+    v_in = F.e2m1_decode(F.unpack_codes(packed)) * np.exp2(np.repeat(sb.astype(np.float64) - 127, 32, axis=1))
+    v_out = F.e4m3_decode(out) * np.repeat(sc.astype(np.float64), 128, axis=1)
+    np.testing.assert_array_equal(v_in, v_out)
+    # FP8 rows with 4-byte scales per 128 values: (1 + 4/128) bytes per value,
+    # the MoE report's 1.03 M K ("通信量")
+    assert (out.nbytes + sc.nbytes) / (T * H) == 1 + 4 / 128
