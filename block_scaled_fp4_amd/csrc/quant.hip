@@ -441,7 +441,7 @@ __global__ __launch_bounds__(kThreads) void ef_qdq_kernel(
     const void* x, float* __restrict__ res, void* y, int64_t n_oct,
     const float* __restrict__ st_ptr, uint64_t seed, uint64_t step, uint32_t* __restrict__ packed,
     uint8_t* __restrict__ scales) {
-  constexpr int U = 2;
+  constexpr int U = 1;   // one octet per thread measured fastest (loads of x and r in flight)
   const float st = *st_ptr;
   const bool newton = nv_newton_range(st);
   const float rst = newton ? 1.0f / st : 0.0f;
@@ -544,7 +544,7 @@ template <bool BF16IN, bool BF16OUT>
 void launch_ef_t(bool res, bool sr, bool codes, const void* x, float* r, void* y, int64_t n_oct,
                  const float* ts, uint64_t seed, uint64_t step, uint32_t* packed, uint8_t* scales,
                  hipStream_t st) {
-  const dim3 g((unsigned)blocks_for(n_oct, 2));
+  const dim3 g((unsigned)blocks_for(n_oct, 1));
 #define FP4MI_EF(RES, SR, CODES)                                                                 \
   hipLaunchKernelGGL((ef_qdq_kernel<BF16IN, BF16OUT, RES, SR, CODES>), g, dim3(kThreads),      \
                      0, st, x, r, y, n_oct, ts, seed, step, packed, scales)
