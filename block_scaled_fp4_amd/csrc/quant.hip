@@ -357,16 +357,18 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(
 // --------------------------------------------------- tensor amax (NVFP4)
 __global__ void zero_u32_kernel(uint32_t* p) { *p = 0u; }
 
-// max |x (+ r)| over the tensor into *out_bits.  The maximum of
-// non-negative floats is taken on their bit patterns (which order like the
-// values; bf16 magnitudes as 16-bit patterns).  Every atomic max on the one
-// word is serialised at the memory side (several ns each), so the grid is
-// kept to at most kAmaxGrid large workgroups, each with U octets per thread
-// in flight, and each workgroup issues a single atomic.
+// max |x (+ r)| over the tensor.  The maximum of non-negative floats is
+// taken on their bit patterns (which order like the values; bf16 magnitudes
+// as 16-bit patterns).  At most kAmaxGrid large workgroups, each with U
+// octets per thread in flight.  PART: workgroup b writes its maximum to
+// out_bits[b] (a caller-side output buffer lent as scratch; a finalize
+// kernel reduces them).  Otherwise each workgroup issues one atomic max on
+// *out_bits, which must start at 0 (atomics on one word are serialised at
+// the memory side, several ns each).
 constexpr int kAmaxThreads = 1024;
 constexpr int kAmaxGrid = 256;
 
-template <bool BF16, bool RES>
+template <bool BF16, bool RES, bool PART>
 __global__ __launch_bounds__(kAmaxThreads) void amax_kernel(const void* __restrict__ x,
                                                             const float* __restrict__ r,
                                                             int64_t n_oct,
@@ -424,7 +426,26 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_kernel(const void* __restri
   if (threadIdx.x == 0) {
     uint32_t q = part[0];
     for (int w = 1; w < kAmaxThreads / 64; ++w) q = max(q, part[w]);
-    atomicMax(out_bits, q);
+    if constexpr (PART) out_bits[blockIdx.x] = q;
+    else atomicMax(out_bits, q);
+  }
+}
+
+// S_t = fl32(A / 2688) (1 when that is 0) from the amax bits of `count`
+// partial maxima; one workgroup of kAmaxGrid threads.
+__global__ __launch_bounds__(kAmaxGrid) void tensor_scale_from_partials_kernel(
+    const uint32_t* __restrict__ parts, int count, float* __restrict__ ts) {
+  __shared__ uint32_t wmax[kAmaxGrid / 64];
+  uint32_t m = threadIdx.x < (unsigned)count ? parts[threadIdx.x] : 0u;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t q = wmax[0];
+    for (int w = 1; w < kAmaxGrid / 64; ++w) q = max(q, wmax[w]);
+    const float s = __uint_as_float(q) / 2688.0f;
+    *ts = (s == 0.0f) ? 1.0f : s;
   }
 }
 
@@ -506,22 +527,32 @@ __global__ __launch_bounds__(kThreads) void ef_qdq_kernel(
 }
 
 // ------------------------------------------------------------ launchers
+// S_t into *ts.  With `scratch` (an output buffer of the call that is
+// written only after S_t is known, of scratch_bytes bytes) the workgroups'
+// maxima go there and one finalize kernel reduces them: two launches, no
+// atomics.  Otherwise: zero, atomic maxima, finalize.
 int launch_tensor_scale(const void* x, bool bf16, const float* res, int64_t n_oct, float* ts,
-                        hipStream_t st) {
-  hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(1), 0, st, reinterpret_cast<uint32_t*>(ts));
+                        void* scratch, int64_t scratch_bytes, hipStream_t st) {
   const int u = (bf16 && !res) ? 4 : 2;
   int64_t g = (n_oct + (int64_t)kAmaxThreads * u - 1) / ((int64_t)kAmaxThreads * u);
   if (g > kAmaxGrid) g = kAmaxGrid;
   const dim3 grid((unsigned)g), blk(kAmaxThreads);
-  uint32_t* bits = reinterpret_cast<uint32_t*>(ts);
-  if (bf16) {
-    if (res) hipLaunchKernelGGL((amax_kernel<true, true>), grid, blk, 0, st, x, res, n_oct, bits);
-    else     hipLaunchKernelGGL((amax_kernel<true, false>), grid, blk, 0, st, x, res, n_oct, bits);
+  const bool part = scratch != nullptr && scratch_bytes >= 4 * g;
+  uint32_t* bits = part ? static_cast<uint32_t*>(scratch) : reinterpret_cast<uint32_t*>(ts);
+  if (!part) hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(1), 0, st, bits);
+#define FP4MI_AMAX(B, R, P) \
+  hipLaunchKernelGGL((amax_kernel<B, R, P>), grid, blk, 0, st, x, res, n_oct, bits)
+  if (part) {
+    if (bf16) { if (res) FP4MI_AMAX(true, true, true); else FP4MI_AMAX(true, false, true); }
+    else      { if (res) FP4MI_AMAX(false, true, true); else FP4MI_AMAX(false, false, true); }
+    hipLaunchKernelGGL(tensor_scale_from_partials_kernel, dim3(1), dim3(kAmaxGrid), 0, st, bits,
+                       (int)g, ts);
   } else {
-    if (res) hipLaunchKernelGGL((amax_kernel<false, true>), grid, blk, 0, st, x, res, n_oct, bits);
-    else     hipLaunchKernelGGL((amax_kernel<false, false>), grid, blk, 0, st, x, res, n_oct, bits);
+    if (bf16) { if (res) FP4MI_AMAX(true, true, false); else FP4MI_AMAX(true, false, false); }
+    else      { if (res) FP4MI_AMAX(false, true, false); else FP4MI_AMAX(false, false, false); }
+    hipLaunchKernelGGL(tensor_scale_finalize_kernel, dim3(1), dim3(1), 0, st, ts);
   }
-  hipLaunchKernelGGL(tensor_scale_finalize_kernel, dim3(1), dim3(1), 0, st, ts);
+#undef FP4MI_AMAX
   return launch_status();
 }
 
@@ -594,7 +625,9 @@ extern "C" int fp4_quantize(const void* x, int dtype, int64_t rows, int64_t cols
   const int64_t n_oct = n / 8;
   if (!grid_fits(n_oct)) return FP4_ESHAPE;
   if (!mx && tscale_mode == FP4_TSCALE_COMPUTE) {
-    int rc = launch_tensor_scale(x, bf16, nullptr, n_oct, tensor_scale, st);
+    // the packed codes are written only after S_t: their buffer holds the
+    // amax pass's partial maxima meanwhile
+    int rc = launch_tensor_scale(x, bf16, nullptr, n_oct, tensor_scale, packed, pb, st);
     if (rc) return rc;
   }
   uint32_t* pk = reinterpret_cast<uint32_t*>(packed);
@@ -681,7 +714,8 @@ extern "C" int fp4_errfeedback_qdq(const void* x, int dtype, int64_t rows, int64
   const int64_t n_oct = n / 8;
   if (!grid_fits(n_oct)) return FP4_ESHAPE;
   if (tscale_mode == FP4_TSCALE_COMPUTE) {
-    int rc = launch_tensor_scale(x, bf16, residual, n_oct, tensor_scale, st);
+    int rc = launch_tensor_scale(x, bf16, residual, n_oct, tensor_scale, packed,
+                                 packed ? n / 2 : 0, st);
     if (rc) return rc;
   }
   uint32_t* pk = reinterpret_cast<uint32_t*>(packed);
