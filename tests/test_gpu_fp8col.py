@@ -104,3 +104,38 @@ def test_full_size_zipf_shards_sampled_experts():
             np.testing.assert_array_equal(got.reshape(-1), ro)
             gs = s[HB * a: HB * b].reshape(HB, n)[blk]
             np.testing.assert_array_equal(gs.view(np.uint32), rs.view(np.uint32))
+
+
+@pytest.mark.parametrize("E", [2047, 2048, 2600])
+def test_expert_table_in_lds_and_in_global_memory(E):
+    """Up to 2047 experts the expert lookups read a table in LDS, beyond that
+    global memory; both sides of the switch, with many tiny and empty
+    experts (so that tiles meet up to 17 experts) and an odd block count."""
+    m = need_gpu()
+    H = 384
+    rng = np.random.default_rng(E)
+    counts = rng.integers(0, 7, size=E)
+    counts[rng.choice(E, 12, replace=False)] = rng.integers(200, 600, size=12)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    T = int(off[-1])
+    packed, sb = synth.random_mxfp4(T, H, seed=E)
+    o, s = convert_gpu(m, packed, sb, off, H)
+    ro, rs = fp8col.convert(packed, sb, off, H)
+    np.testing.assert_array_equal(o, ro)
+    np.testing.assert_array_equal(s.view(np.uint32), rs.view(np.uint32))
+
+
+@pytest.mark.parametrize("counts,H", [
+    ([255, 1, 256, 257, 17, 16, 15, 240, 512], 640),      # experts ending on and off tile seams
+    ([4096], 256),                                        # one expert over 17 tiles
+])
+def test_tile_seams(counts, H):
+    m = need_gpu()
+    counts = np.array(counts)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    T = int(off[-1])
+    packed, sb = synth.random_mxfp4(T, H, seed=T)
+    o, s = convert_gpu(m, packed, sb, off, H)
+    ro, rs = fp8col.convert(packed, sb, off, H)
+    np.testing.assert_array_equal(o, ro)
+    np.testing.assert_array_equal(s.view(np.uint32), rs.view(np.uint32))
