@@ -83,16 +83,6 @@ __device__ __forceinline__ NvScale nv_block_scale_newton(float absmax, float st,
   return NvScale{c, e4m3_value_hw(c) * st};
 }
 
-// Block scale by the division-free chain where it holds, else the IEEE one.
-__device__ __forceinline__ NvScale nv_block_scale(float absmax, float st, float rst, bool newton) {
-  if (newton) {
-    bool ok;
-    const NvScale s = nv_block_scale_newton(absmax, st, rst, &ok);
-    if (ok) return s;
-  }
-  return nv_block_scale_exact(absmax, st);
-}
-
 // MXFP4: UE8M0 byte = clamp(floor(log2 absmax) - 2 + 127, 0, 254), read from
 // the exponent field; subnormal and zero maxima give 0.
 __device__ __forceinline__ uint32_t mx_scale_byte(float absmax) {
@@ -166,6 +156,43 @@ __device__ __forceinline__ uint32_t encode_octet_nv_rtn(const float (&v)[8], flo
   return rtn8_unit(q);
 }
 
+// NVFP4 SR codes of q = fl32(v / sdec) (sdec != 0) from the division-free
+// quotient.  With y = fl32(1 / sdec), a one-fma correction of fl32(v y) is
+// the IEEE quotient whenever neither the quotient nor the residual
+// underflows (Markstein's correction theorem); on the GPU it matched the
+// IEEE division for every bf16 numerator significand against every fp32
+// divisor significand, at exponent pairs spanning |v| >= 2^-100, |q| in
+// [2^-100, 2^114] and sdec in [2^-109, 2^109].  The SR decision reads every
+// bit of q, so elements outside that range (|v| or |q| below 2^-100, zero
+// excepted) take the IEEE division.
+__device__ __forceinline__ uint32_t encode_octet_nv_sr_newton(const float (&v)[8], float sdec,
+                                                              int64_t i, uint64_t seed,
+                                                              uint64_t step) {
+  uint32_t u[8];
+  sr_draws8(i, seed, step, u);
+  const float y = recip_rn(sdec);
+  // |v| >= 2^-100 and |v / sdec| >= 2^-100  <=>  |v| >= 2^-100 max(1, sdec)
+  // (a power-of-two multiple of sdec, exact); twice the magnitude bits
+  // minus 2 maps a zero to the top of the unsigned range
+  const uint32_t lim = (__float_as_uint(0x1p-100f * fmaxf(1.0f, sdec)) << 1) - 2u;
+  float q[8];
+  uint32_t small = 0xFFFFFFFFu;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    q[j] = div_rn(v[j], sdec, y);
+    small = min(small, (__float_as_uint(v[j]) << 1) - 2u);
+  }
+  if (small < lim) {                                   // rare: IEEE quotients
+#pragma unroll
+    for (int j = 0; j < 8; ++j) q[j] = v[j] / sdec;
+  }
+  uint32_t word = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    word |= (e2m1_sr_mag(fabsf(q[j]), u[j], false) | sign_nibble(v[j])) << (4 * j);
+  return word;
+}
+
 // MXFP4 RTN codes: divide by 2^e and round in the converter (bf16 words go
 // in unexpanded; fp32 values are scaled exactly first and converted at unit
 // scale).
@@ -226,9 +253,15 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
       if constexpr (SR) word = encode_octet_sw<true, true>(v, 0.0f, 127 - (int)scode, i, seed, step);
       else word = encode_octet_mx_rtn<BF16>(ra[k], v, scode);
     } else if constexpr (SR) {
-      const NvScale s = nv_block_scale(am, st, rst, newton);
+      // bf16 blocks whose scale came from the division-free chain (S_t in
+      // range, raw quotient below 2^120) take division-free element quotients
+      bool ok = false;
+      NvScale s{0u, 0.0f};
+      if (newton) s = nv_block_scale_newton(am, st, rst, &ok);
+      if (!ok) s = nv_block_scale_exact(am, st);
       scode = s.code;
-      word = encode_octet_sw<false, true>(v, s.sdec, 0, i, seed, step);
+      if (BF16 && ok && s.sdec != 0.0f) word = encode_octet_nv_sr_newton(v, s.sdec, i, seed, step);
+      else word = encode_octet_sw<false, true>(v, s.sdec, 0, i, seed, step);
     } else {
       static_assert(MX || SR, "NVFP4 RTN has its own kernel");
     }

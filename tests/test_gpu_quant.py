@@ -331,3 +331,31 @@ def test_empty_tensors_are_noops():
     assert p.numel() == 0 and s.numel() == 0
     y = m.fp4_dequantize(p, s, 0, 64, "mxfp4")
     assert y.numel() == 0
+
+
+@pytest.mark.parametrize("step", [0, 5])
+def test_nvfp4_sr_bf16_every_pattern_given_scales(step):
+    """Stochastic rounding of bf16 input (division-free element quotients,
+    with the IEEE division for elements or quotients below 2^-100): every
+    finite bf16 pattern in blocks anchored to several block scales,
+    including quotients far below 2^-100 and S_t outside [2^-100, 2^100]."""
+    m = need_gpu()
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    x = F.bf16_bits_to_f32(bits)
+    keep = np.isfinite(x)
+    bits, x = bits[keep], x[keep]
+    for st, amax in [(1.0, 6.0), (0.37, 1.875), (2.0 ** -20, 2.0 ** -15), (1e4, 786432.0),
+                     (2.0 ** -110, 2.0 ** -100), (2.0 ** 105, 2.0 ** 110), (3.0e-20, 2.0 ** -40)]:
+        sel = bits[np.abs(x.astype(np.float64)) <= amax]
+        sel = np.concatenate([sel, np.zeros((-sel.size) % 15, np.uint16)]).reshape(-1, 15)
+        a16 = np.uint16(np.float32(amax).view(np.uint32) >> 16)
+        assert F.bf16_bits_to_f32(np.array([a16]))[0] == np.float32(amax)
+        blk = np.concatenate([np.full((sel.shape[0], 1), a16, np.uint16), sel], axis=1).reshape(1, -1)
+        st = np.float32(st)
+        ts = dev_f32(np.array([st], np.float32))
+        p, s, _ = run_quant(m, dev_bf16(blk), "nvfp4", "sr", seed=0x5EED5EED12345, step=step,
+                            tscale="given", ts=ts)
+        rp, rs = nvfp4.quantize_packed(F.bf16_bits_to_f32(blk), st, "sr", seed=0x5EED5EED12345,
+                                       step=step)
+        np.testing.assert_array_equal(s, rs)
+        np.testing.assert_array_equal(p, rp)
