@@ -108,7 +108,7 @@ __device__ __forceinline__ int clampT(int64_t v, int T) {
 }
 
 struct ColPlan {
-  int tile, bp;        // the item
+  int bp;              // block pair of the item
   int off1, n1, u1;    // loader: expert of the lane's 4 positions, first local index
   int off2, n2, u2;    // storer: expert of the lane's chunk, its first local index
 };
@@ -199,7 +199,6 @@ __device__ __forceinline__ ColPlan plan_item(const int64_t* off, const int* offs
     i2 = (q == q2) ? idx : i2;
   }
   ColPlan p;
-  p.tile = tile;
   p.bp = bp;
   p.off1 = __shfl(c_off, i1);
   p.n1 = __shfl(c_n, i1);
@@ -210,12 +209,14 @@ __device__ __forceinline__ ColPlan plan_item(const int64_t* off, const int* offs
   return p;
 }
 
-// Items are numbered tile fastest.  L2 domain x (workgroups x, x + 8, ...)
-// takes items [x ipx, (x + 1) ipx); at step k its workgroup in slot s takes
-// item x ipx + k S + s (S slots per domain), so the S workgroups of a domain
-// convert S consecutive tiles at once: the output sectors that straddle two
-// neighbouring tiles are completed in one L2 before they are written back,
-// instead of reaching HBM as two partial writes.
+// Items are numbered tile fastest.  Workgroups are dispatched to the L2
+// domains round-robin, so domain x holds workgroups x, x + 8, ...; it takes
+// items [x ipx, (x + 1) ipx), and at step k its workgroup in slot s takes
+// item x ipx + k S + s (S slots per domain).  The S workgroups of a domain
+// thus convert S consecutive tiles at about the same time, and the two parts
+// of an output sector that straddles neighbouring tiles mostly meet in that
+// L2 before write-back instead of reaching HBM as two partial writes.  (The
+// dispatch order is a performance assumption only.)
 template <bool LDS_TABLE>
 __global__ __launch_bounds__(kCThreads) void fp8col_tiles_kernel(
     const uint8_t* __restrict__ packed, const uint8_t* __restrict__ sb,

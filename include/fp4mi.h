@@ -182,12 +182,15 @@ int fp4_errfeedback_qdq(const void* x, int dtype, int64_t rows, int64_t cols,
  *  scales_e8m0    [T, H/32] UE8M0 bytes (0xFF outside the contract), 4-byte aligned
  *  token_offsets  device int64 [E+1]: off[0] = 0, nondecreasing, off[E] = T,
  *                 8-byte aligned (contents are not validated on the host)
- *  num_experts    E >= 1;  total_tokens 0 <= T < 2^26;  hidden 0 < H < 2^21, H % 128 == 0
- *  fp8_out        out bytes [T*H]; expert e occupies [H*off[e], H*off[e+1])
- *                 as a dense [H, n_e] matrix
+ *  num_experts    1 <= E < 2^26 (FP4_EINVAL below 1, FP4_ESHAPE from 2^26);
+ *                 total_tokens 0 <= T < 2^26;  hidden 0 < H < 2^21, H % 128 == 0
+ *  fp8_out        out bytes [T*H], 4-byte aligned; expert e occupies
+ *                 [H*off[e], H*off[e+1]) as a dense [H, n_e] matrix
  *  fp8_scales     out fp32 [T*H/128]; expert e occupies
  *                 [(H/128)*off[e], (H/128)*off[e+1]) as [H/128, n_e]; 4-byte aligned
- * Outputs must not overlap inputs.
+ * Outputs must not overlap inputs (FP4_EOVERLAP).  Malformed offsets (not
+ * ascending, outside [0, T]) are clamped on the device: the outputs are then
+ * unspecified but every access stays inside the buffers.
  */
 int mxfp4_row_to_fp8_col(const uint8_t* packed, const uint8_t* scales_e8m0,
                          const int64_t* token_offsets, int32_t num_experts,

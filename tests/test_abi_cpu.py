@@ -116,6 +116,8 @@ def test_other_entry_points_validation(lib):
     assert cv(A, A + (1 << 30), A + (2 << 30), 4, 64, 200, A + (3 << 30), A + (4 << 30), None) == c["FP4_ESHAPE"]
     assert cv(A, A + (1 << 30), A + (2 << 30), 4, 1 << 26, 128, A + (3 << 30), A + (4 << 30),
               None) == c["FP4_ESHAPE"]                          # tokens limited to 2^26 - 1
+    assert cv(A, A + (1 << 30), A + (2 << 30), 1 << 26, 64, 128, A + (3 << 30), A + (4 << 30),
+              None) == c["FP4_ESHAPE"]                          # experts limited to 2^26 - 1
     assert cv(A + 4, A + (1 << 30), A + (2 << 30), 4, 64, 256, A + (3 << 30), A + (4 << 30), None) == c["FP4_EALIGN"]
     assert cv(A, A + (1 << 30), A + (2 << 30), 4, 64, 256, A + 100, A + (4 << 30), None) == c["FP4_EOVERLAP"]
     assert cv(A, A + (1 << 30), A + (2 << 30), 4, 0, 256, A + (3 << 30), A + (4 << 30), None) == c["FP4_OK"]
