@@ -1,0 +1,134 @@
+"""Seeded random sweep of fp4_quantize / fp4_dequantize against the oracle:
+random shapes (ragged rows, several block rows), random value mixes (heavy
+tails, exact zeros and negative zeros, tiny and large magnitudes, per-row
+exponent spread) over every format x rounding x input dtype x tensor-scale
+mode.  Bit-exact codes, scales, tensor scale and dequantized values."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import Guarded, dev_bf16, dev_f32, host, host_bf16, need_gpu
+from oracle import formats as F
+from oracle import mxfp4, nvfp4
+
+pytestmark = pytest.mark.gpu
+
+
+def _values(rng, rows, cols):
+    x = rng.standard_t(2.5, size=(rows, cols)) * np.exp2(rng.integers(-40, 40, size=(rows, 1)))
+    r = rng.random((rows, cols))
+    x[r < 0.03] = 0.0
+    x[(r >= 0.03) & (r < 0.05)] = -0.0
+    x[(r >= 0.05) & (r < 0.06)] *= 2.0 ** -90
+    x[(r >= 0.06) & (r < 0.07)] *= 2.0 ** 60
+    return x.astype(np.float32)
+
+
+def _cases():
+    out = []
+    rng = np.random.default_rng(2024)
+    for fmt in ("nvfp4", "mxfp4"):
+        for rounding in ("rtn", "sr"):
+            for dtype in ("bf16", "f32"):
+                for tscale in (("compute", "given") if fmt == "nvfp4" else ("compute",)):
+                    for _ in range(2):
+                        rows = int(rng.integers(1, 300))
+                        cols = 32 * int(rng.integers(1, 64))
+                        out.append((fmt, rounding, dtype, tscale, rows, cols, int(rng.integers(1 << 30))))
+    return out
+
+
+@pytest.mark.parametrize("fmt,rounding,dtype,tscale,rows,cols,seed", _cases())
+def test_random_quantize_dequantize(fmt, rounding, dtype, tscale, rows, cols, seed):
+    m = need_gpu()
+    rng = np.random.default_rng(seed)
+    x = _values(rng, rows, cols)
+    if dtype == "bf16":
+        xb = F.f32_to_bf16_bits(x)
+        x = F.bf16_bits_to_f32(xb)
+        x_dev = dev_bf16(xb)
+    else:
+        x_dev = dev_f32(x)
+    blk = 16 if fmt == "nvfp4" else 32
+    sr_seed, step = int(rng.integers(1 << 62)), int(rng.integers(1 << 40))
+    if fmt == "nvfp4":
+        st = nvfp4.tensor_scale(x) if tscale == "compute" else np.float32(rng.uniform(1e-3, 10.0))
+    gp, gs = Guarded(rows * cols // 2), Guarded(rows * cols // blk)
+    ts = dev_f32(np.array([0.0 if fmt == "mxfp4" or tscale == "compute" else st], np.float32))
+    p, s, ts_out = m.fp4_quantize(x_dev, fmt, rounding, sr_seed, step, tscale,
+                                  ts if fmt == "nvfp4" else None,
+                                  gp.view(torch.uint8, (rows, cols // 2)),
+                                  gs.view(torch.uint8, (rows, cols // blk)))
+    torch.cuda.synchronize()
+    gp.check()
+    gs.check()
+    p, s = host(p), host(s)
+    if fmt == "nvfp4":
+        assert np.float32(host(ts_out)[0]) == np.float32(st)
+        rp, rs = nvfp4.quantize_packed(x, np.float32(st), rounding, seed=sr_seed, step=step)
+    else:
+        rp, rs = mxfp4.quantize_packed(x, rounding, seed=sr_seed, step=step)
+    np.testing.assert_array_equal(s, rs)
+    np.testing.assert_array_equal(p, rp)
+    for out in (torch.bfloat16, torch.float32):
+        es = 2 if out == torch.bfloat16 else 4
+        gy = Guarded(rows * cols * es)
+        y = m.fp4_dequantize(torch.from_numpy(p).cuda(), torch.from_numpy(s).cuda(), rows, cols, fmt,
+                             dev_f32(np.array([st], np.float32)) if fmt == "nvfp4" else None, out,
+                             gy.view(out, (rows, cols)))
+        torch.cuda.synchronize()
+        gy.check()
+        kind = "bf16" if out == torch.bfloat16 else "f32"
+        if fmt == "nvfp4":
+            ref = nvfp4.dequantize(rp, rs, np.float32(st), kind)
+        else:
+            ref = mxfp4.dequantize(rp, rs, kind)
+        got = host_bf16(y) if out == torch.bfloat16 else host(y)
+        if out == torch.bfloat16:
+            np.testing.assert_array_equal(got, ref)
+        else:
+            np.testing.assert_array_equal(got.view(np.uint32), np.asarray(ref, np.float32).view(np.uint32))
+
+
+def _fp8_cases():
+    rng = np.random.default_rng(77)
+    shapes = [(1, 896), (3, 384), (40, 896), (300, 256), (2100, 128), (3, 1024), (40, 512), (300, 640)]
+    return [(E, H, int(rng.integers(1 << 30))) for E, H in shapes]
+
+
+@pytest.mark.parametrize("E,H,seed", _fp8_cases())
+def test_random_fp8_row_and_column(E, H, seed):
+    """Random expert counts (geometric, with empty experts and a few large
+    ones) and hidden sizes: FP8 rows and per-expert FP8 columns, bit-exact."""
+    from oracle import fp8col
+    import synth
+    m = need_gpu()
+    rng = np.random.default_rng(seed)
+    counts = rng.geometric(0.25, size=E) - 1
+    counts[rng.random(E) < 0.2] = 0
+    big = rng.random(E) < (0.5 if E < 10 else 0.01)
+    counts[big] = rng.integers(200, 700, size=int(big.sum()))
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    T = int(off[-1])
+    if T == 0:
+        pytest.skip("no tokens drawn")
+    packed, sb = synth.random_mxfp4(T, H, seed=seed, scale_lo=100, scale_hi=150)
+    go, gs = Guarded(T * H), Guarded(T * H // 128 * 4)
+    o, s = m.mxfp4_row_to_fp8_col(torch.from_numpy(packed).cuda(), torch.from_numpy(sb).cuda(),
+                                  torch.from_numpy(off).cuda(), H, go.view(torch.uint8, (T * H,)),
+                                  gs.view(torch.float32, (T * H // 128,)))
+    torch.cuda.synchronize()
+    go.check()
+    gs.check()
+    ro, rs = fp8col.convert(packed, sb, off, H)
+    np.testing.assert_array_equal(host(o), ro)
+    np.testing.assert_array_equal(host(s).view(np.uint32), rs.view(np.uint32))
+    gr, grs = Guarded(T * H), Guarded(T * H // 128 * 4)
+    r, rsc = m.mxfp4_row_to_fp8_row(torch.from_numpy(packed).cuda(), torch.from_numpy(sb).cuda(), H,
+                                    gr.view(torch.uint8, (T, H)), grs.view(torch.float32, (T, H // 128)))
+    torch.cuda.synchronize()
+    gr.check()
+    grs.check()
+    qo, qs = fp8col.convert_rows(packed, sb, H)
+    np.testing.assert_array_equal(host(r), qo)
+    np.testing.assert_array_equal(host(rsc).view(np.uint32), qs.view(np.uint32))
