@@ -7,11 +7,11 @@
 // FP8 columns.  Expert e occupies positions poff(e) = 16 (ceil(off_e / 16) +
 // e) .. poff(e) + n_e - 1 of a padded position space: every expert starts on
 // a multiple of 16 and owns at least 16 positions, so each 16-position chunk
-// lies in one expert and a 256-position tile meets at most 17 experts.  poff
+// lies in one expert and a 512-position tile meets at most 33 experts.  poff
 // is a closed form of off_e and e (no prefix sum over the experts).
 //
-// A work item is (tile of 256 positions, pair of 128-channel blocks), taken
-// by a workgroup of 8 waves:
+// A work item is (tile of 512 positions, pair of 128-channel blocks), taken
+// by a workgroup of 16 waves (one per CU: its LDS tile is 128 KB):
 //   1. lane l of wave w loads, for sub-block s8 = l mod 8 of the pair, the 16
 //      code bytes and the block's four UE8M0 bytes of the 4 positions 4 g ..
 //      4 g + 3, g = 8 w + l / 8: eight neighbouring lanes read one token's
@@ -20,9 +20,9 @@
 //      table per shift d (v_perm_b32 does 4 lookups at once; the tables come
 //      from the exponent-field mapping E8 = E4 - 1 + 7 - d).  4 x 4 byte
 //      blocks are transposed inside the lane, and each channel's dword of 4
-//      positions goes to LDS, [256 rows][64 dwords], with the columns of each
+//      positions goes to LDS, [256 rows][128 dwords], with the columns of each
 //      sub-block XOR-swizzled so that every write is bank-conflict-free;
-//   2. after a barrier, wave w reads rows 32 w .. 32 w + 31, one 16-byte chunk
+//   2. after a barrier, wave w reads rows 16 w .. 16 w + 15, one 16-byte chunk
 //      per lane, and writes it with one unaligned 16-byte store at
 //      H off_e + h n_e + u.  Stores are byte-masked, so chunks of neighbouring
 //      tiles and experts meet without stitching; the last chunk of an expert
@@ -30,8 +30,8 @@
 // Output rows start at any byte, so the 64-byte sectors at tile seams are
 // written in two parts by two tiles.  HBM takes a partial sector at about
 // half the rate of a whole one unless the two parts meet in an L2 first, so
-// the workgroups of one L2 domain convert neighbouring tiles together (see
-// fp8col_tiles_kernel).  Offsets are clamped to [0, T]; with malformed
+// tiles are long (512 bytes of each row) and the workgroups of one L2 domain
+// convert neighbouring tiles together (see fp8col_tiles_kernel).  Offsets are clamped to [0, T]; with malformed
 // (non-ascending) offsets every access still stays inside the buffers.
 #include "device_common.hpp"
 #include "host_common.hpp"
@@ -86,8 +86,8 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-constexpr int kCTile = 256;                 // positions per tile
-constexpr int kCThreads = 512;              // 8 waves: 2 blocks x 4 sub-blocks
+constexpr int kCTile = 512;                 // positions per tile
+constexpr int kCThreads = 1024;             // 16 waves
 constexpr int kCRowDw = kCTile / 4;         // dwords per LDS row
 
 typedef uint32_t u32x4_ua __attribute__((ext_vector_type(4), aligned(1)));
@@ -96,8 +96,9 @@ typedef uint32_t u32_ua __attribute__((aligned(1)));
 typedef uint16_t u16_ua __attribute__((aligned(1)));
 
 // Column swizzle of the LDS rows of sub-block s8 (0..7 over the block pair):
-// XOR with 8 s8 + 4 (s8 / 4) dwords.  A ds_write_b32 of a wave covers 8 rows
-// (one per s8) x 8 consecutive columns; the XOR gives the 8 rows distinct
+// XOR with 8 s8 + 4 (s8 / 4) dwords (the row pitch is a multiple of 64
+// dwords).  A ds_write_b32 of a wave covers 8 rows (one per s8) x 8
+// consecutive columns; the XOR gives the 8 rows distinct
 // 8-dword groups mod 64 and, for each half wave, distinct 4-dword groups
 // mod 32, so it is conflict-free with 64 or 32 banks.  Multiples of 4 keep
 // every 16-byte chunk contiguous.
@@ -192,7 +193,7 @@ __device__ __forceinline__ ColPlan plan_item(const int64_t* off, const int* offs
   }
   int i1 = 0, i2 = 0;
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
+  for (int q = 0; q < kCTile / 16; ++q) {
     const uint64_t m = __ballot(c_poff <= P0 + 16 * q);
     const int idx = m ? 63 - __builtin_clzll(m) : 0;
     i1 = (q == q1) ? idx : i1;
@@ -227,8 +228,8 @@ __global__ __launch_bounds__(kCThreads) void fp8col_tiles_kernel(
   __shared__ int offs[LDS_TABLE ? kOffLds : 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // loader role: sub-block s8 of the pair, positions 4 g .. 4 g + 3 of the tile;
-  // storer role: LDS rows 32 wave .. 32 wave + 31 (sub-block s8 = wave)
-  const int s8 = lane & 7, g = 8 * wave + (lane >> 3), q1 = g >> 2, q2 = lane & 15;
+  // storer role: LDS rows 16 wave .. 16 wave + 15 (sub-block s8 = wave / 2)
+  const int s8 = lane & 7, g = 8 * wave + (lane >> 3), q1 = g >> 2, q2 = lane & 31;
   const int64_t HB = H / 128;
   const int xcd = (int)(blockIdx.x % kXcds), slot = (int)(blockIdx.x / kXcds);
   const int64_t i0 = xcd * ipx, i1 = min(i0 + ipx, nitems);
@@ -301,17 +302,17 @@ __global__ __launch_bounds__(kCThreads) void fp8col_tiles_kernel(
         sc_out[HB * cur.off1 + b * cur.n1 + u] = __builtin_amdgcn_ldexpf(1.0f, (int)tgt_s - 127);
     }
     lds_barrier();
-    // rows 32 wave .. 32 wave + 31, one 16-byte chunk per lane
+    // rows 16 wave .. 16 wave + 15, one 16-byte chunk per lane
     {
-      const bool blk_ok = 2 * (int64_t)cur.bp + (wave >> 2) < HB;
+      const bool blk_ok = 2 * (int64_t)cur.bp + (wave >> 3) < HB;
       const int L = (blk_ok && cur.u2 >= 0) ? min(max(cur.n2 - cur.u2, 0), 16) : 0;
       const int64_t rowbase = H * (int64_t)cur.off2 + cur.u2;
-      const uint32_t* src = tile + (32 * wave + (lane >> 4)) * kCRowDw +
-                            ((4 * q2) ^ col_swz(wave));
+      const uint32_t* src = tile + (16 * wave + (lane >> 5)) * kCRowDw +
+                            ((4 * q2) ^ col_swz(wave >> 1));
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(src + 4 * k * kCRowDw);
-        const int64_t h = 256 * (int64_t)cur.bp + 32 * wave + 4 * k + (lane >> 4);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(src + 2 * k * kCRowDw);
+        const int64_t h = 256 * (int64_t)cur.bp + 16 * wave + 2 * k + (lane >> 5);
         uint8_t* dst = out + rowbase + h * cur.n2;
         if (L == 16) *reinterpret_cast<u32x4_ua*>(dst) = v;
         else if (L > 0) store_partial(dst, v, L);
@@ -335,9 +336,10 @@ int launch_fp8col_tiles(const uint8_t* packed, const uint8_t* sb, const int64_t*
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess)
     (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  // two resident workgroups per CU, spread over the L2 domains
+  // one resident workgroup per CU (its LDS tile is 128 KB), spread over the
+  // L2 domains
   const int64_t ipx = (nitems + kXcds - 1) / kXcds;
-  int64_t slots = max((int64_t)(2 * max(cus, 1) / kXcds), (int64_t)1);
+  int64_t slots = max((int64_t)(max(cus, 1) / kXcds), (int64_t)1);
   if (slots > ipx) slots = ipx;
   const unsigned grid = (unsigned)(kXcds * slots);
   if (E + 1 <= kOffLds)

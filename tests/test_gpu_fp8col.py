@@ -110,7 +110,7 @@ def test_full_size_zipf_shards_sampled_experts():
 def test_expert_table_in_lds_and_in_global_memory(E):
     """Up to 2047 experts the expert lookups read a table in LDS, beyond that
     global memory; both sides of the switch, with many tiny and empty
-    experts (so that tiles meet up to 17 experts) and an odd block count."""
+    experts (so that tiles meet many experts) and an odd block count."""
     m = need_gpu()
     H = 384
     rng = np.random.default_rng(E)
@@ -126,8 +126,9 @@ def test_expert_table_in_lds_and_in_global_memory(E):
 
 
 @pytest.mark.parametrize("counts,H", [
-    ([255, 1, 256, 257, 17, 16, 15, 240, 512], 640),      # experts ending on and off tile seams
-    ([4096], 256),                                        # one expert over 17 tiles
+    ([255, 1, 256, 257, 17, 16, 15, 240, 512], 640),      # experts ending on and off 256-seams
+    ([511, 1, 512, 513, 33, 32, 31, 496, 1024], 384),     # and on and off 512-position seams
+    ([8200], 256),                                        # one expert over 17 tiles
 ])
 def test_tile_seams(counts, H):
     m = need_gpu()
