@@ -243,12 +243,16 @@ __device__ __forceinline__ void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32
 
 // Eight uniform 24-bit draws for elements 8*i .. 8*i+7 of the stream keyed by
 // (seed, step): element j uses counter (j>>2, step) and output word j & 3.
+// WIDE = false promises 2 i + 1 < 2^32 (the counter's second word is then 0,
+// so the first rounds' second products depend only on seed and step and are
+// computed once per wave on the scalar unit).
+template <bool WIDE = true>
 __device__ __forceinline__ void sr_draws8(int64_t i, uint64_t seed, uint64_t step,
                                           uint32_t (&u)[8]) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     uint64_t blk = (uint64_t)i * 2u + (uint64_t)h;
-    uint32_t c0 = (uint32_t)blk, c1 = (uint32_t)(blk >> 32);
+    uint32_t c0 = (uint32_t)blk, c1 = WIDE ? (uint32_t)(blk >> 32) : 0u;
     uint32_t c2 = (uint32_t)step, c3 = (uint32_t)(step >> 32);
     philox4x32_10(c0, c1, c2, c3, (uint32_t)seed, (uint32_t)(seed >> 32));
     u[4 * h + 0] = c0 >> 8; u[4 * h + 1] = c1 >> 8;

@@ -118,11 +118,11 @@ __device__ __forceinline__ void load_octet(const void* x, int64_t i, float (&v)[
 }
 
 // Codes of one octet under a decided block scale (software rounding; exact).
-template <bool MX, bool SR>
+template <bool MX, bool SR, bool WIDE = true>
 __device__ __forceinline__ uint32_t encode_octet_sw(const float (&v)[8], float sdec, int mx_shift,
                                                     int64_t i, uint64_t seed, uint64_t step) {
   uint32_t u[8];
-  if constexpr (SR) sr_draws8(i, seed, step, u);
+  if constexpr (SR) sr_draws8<WIDE>(i, seed, step, u);
   uint32_t word = 0;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -165,11 +165,12 @@ __device__ __forceinline__ uint32_t encode_octet_nv_rtn(const float (&v)[8], flo
 // [2^-100, 2^114] and sdec in [2^-109, 2^109].  The SR decision reads every
 // bit of q, so elements outside that range (|v| or |q| below 2^-100, zero
 // excepted) take the IEEE division.
+template <bool WIDE>
 __device__ __forceinline__ uint32_t encode_octet_nv_sr_newton(const float (&v)[8], float sdec,
                                                               int64_t i, uint64_t seed,
                                                               uint64_t step) {
   uint32_t u[8];
-  sr_draws8(i, seed, step, u);
+  sr_draws8<WIDE>(i, seed, step, u);
   const float y = recip_rn(sdec);
   // |v| >= 2^-100 and |v / sdec| >= 2^-100  <=>  |v| >= 2^-100 max(1, sdec)
   // (a power-of-two multiple of sdec, exact); twice the magnitude bits
@@ -217,7 +218,7 @@ __device__ __forceinline__ uint32_t encode_octet_mx_rtn(const u32x4& raw, const 
 // Thread t of workgroup b owns octets b*256*U + t + 256*k, k < U: every
 // load and store instruction of a wave covers 64 consecutive octets, and
 // the U loads are issued before any of them is consumed.
-template <bool BF16, bool MX, bool SR, int U = kOctets<BF16>>
+template <bool BF16, bool MX, bool SR, int U = kOctets<BF16>, bool WIDE = true>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(
     const void* __restrict__ x, int64_t n_oct, const float* __restrict__ st_ptr, uint64_t seed,
     uint64_t step, uint32_t* __restrict__ packed, uint8_t* __restrict__ scales) {
@@ -250,7 +251,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
     uint32_t scode, word;
     if constexpr (MX) {
       scode = mx_scale_byte(am);
-      if constexpr (SR) word = encode_octet_sw<true, true>(v, 0.0f, 127 - (int)scode, i, seed, step);
+      if constexpr (SR)
+        word = encode_octet_sw<true, true, WIDE>(v, 0.0f, 127 - (int)scode, i, seed, step);
       else word = encode_octet_mx_rtn<BF16>(ra[k], v, scode);
     } else if constexpr (SR) {
       // bf16 blocks whose scale came from the division-free chain (S_t in
@@ -260,8 +262,10 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
       if (newton) s = nv_block_scale_newton(am, st, rst, &ok);
       if (!ok) s = nv_block_scale_exact(am, st);
       scode = s.code;
-      if (BF16 && ok && s.sdec != 0.0f) word = encode_octet_nv_sr_newton(v, s.sdec, i, seed, step);
-      else word = encode_octet_sw<false, true>(v, s.sdec, 0, i, seed, step);
+      if (BF16 && ok && s.sdec != 0.0f)
+        word = encode_octet_nv_sr_newton<WIDE>(v, s.sdec, i, seed, step);
+      else
+        word = encode_octet_sw<false, true, WIDE>(v, s.sdec, 0, i, seed, step);
     } else {
       static_assert(MX || SR, "NVFP4 RTN has its own kernel");
     }
@@ -593,7 +597,11 @@ template <bool BF16, bool MX>
 void launch_quantize_t(bool sr, const void* x, int64_t n_oct, const float* ts, uint64_t seed,
                        uint64_t step, uint32_t* packed, uint8_t* scales, hipStream_t st) {
   const dim3 g((unsigned)blocks_for(n_oct, kOctets<BF16>));
-  if (sr)
+  // SR counters 2 i + 1 below 2^32: their second word is 0 throughout
+  if (sr && 2 * n_oct <= (int64_t(1) << 32))
+    hipLaunchKernelGGL((quantize_kernel<BF16, MX, true, kOctets<BF16>, false>), g, dim3(kThreads),
+                       0, st, x, n_oct, ts, seed, step, packed, scales);
+  else if (sr)
     hipLaunchKernelGGL((quantize_kernel<BF16, MX, true>), g, dim3(kThreads), 0, st, x, n_oct,
                        ts, seed, step, packed, scales);
   else if (MX)
