@@ -75,8 +75,10 @@ extern "C" {
  *  fmt          FP4_FMT_NVFP4 or FP4_FMT_MXFP4
  *  rounding     FP4_ROUND_RTN or FP4_ROUND_SR; seed and step key the SR stream
  *  tscale_mode  NVFP4 only.  COMPUTE: S_t = max|x| / 2688 (1 if that is 0) is
- *               computed and written to *tensor_scale.  GIVEN: *tensor_scale
- *               (a positive finite fp32) is read.  Ignored for MXFP4.
+ *               computed and written to *tensor_scale (a pass over x before
+ *               the codes; the packed output holds its partial maxima until
+ *               the codes overwrite them).  GIVEN: *tensor_scale (a positive
+ *               finite fp32) is read.  Ignored for MXFP4.
  *  tensor_scale device fp32, 4-byte aligned; may be NULL for MXFP4
  *  packed       out [rows, cols/2] bytes, 4-byte aligned
  *  scales       out: NVFP4 [rows, cols/16] E4M3 bytes, MXFP4 [rows, cols/32]
@@ -157,7 +159,8 @@ int fp4quant_decode(const uint8_t* packed, const float* s_rms, const float* s_ab
  *                out_dtype == dtype (in-place weight update); otherwise no
  *                overlap with the inputs
  *  packed,scales optional outputs (NULL to skip), layouts as fp4_quantize
- *  tensor_scale  device fp32, written (COMPUTE) or read (GIVEN)
+ *  tensor_scale  device fp32, written (COMPUTE) or read (GIVEN); COMPUTE
+ *                uses packed (when given) for partial maxima before the codes
  */
 int fp4_errfeedback_qdq(const void* x, int dtype, int64_t rows, int64_t cols,
                         float* residual, void* y, int out_dtype,
