@@ -1,0 +1,112 @@
+"""CPU model of the FP8-column kernel's index arithmetic (expert search,
+candidate experts, per-lane plans, load and store ranges), run on
+well-formed and malformed token offsets: every load of codes and scales and
+every store of FP8 bytes and fp32 scales must stay inside its buffer.  The
+model follows the kernel's integer steps: padded starts 16 (ceil(off / 16) +
+e) of clamped offsets, a 64-way search per tile, 64 candidate experts, the
+last candidate at or before each 16-position chunk."""
+import numpy as np
+import pytest
+
+TILE = 512
+CHUNKS = TILE // 16
+
+
+def clampT(v, T):
+    return np.minimum(np.maximum(v, 0), T)
+
+
+def poff(offc, e):
+    return 16 * ((offc[e] + 15) // 16 + e)
+
+
+def find_expert(offc, E, P):
+    lo, hi = 0, E
+    while hi - lo > 1:
+        step = (hi - lo + 63) // 64
+        e = lo + np.arange(64) * step
+        ok = e < hi
+        le = np.zeros(64, bool)
+        le[ok] = poff(offc, e[ok]) <= P
+        last = int(np.nonzero(le)[0].max()) if le.any() else 0
+        lo += last * step
+        hi = min(lo + step, hi)
+    return lo
+
+
+def check_bounds(off, T, H):
+    E = len(off) - 1
+    offc = clampT(np.asarray(off, np.int64), T)
+    ptot = 16 * ((T + 15) // 16 + E)
+    ntiles = (ptot + TILE - 1) // TILE
+    HB = H // 128
+    npairs = (HB + 1) // 2
+    code_bytes, scale_bytes, out_bytes, sc_floats = T * H // 2, T * H // 32, T * H, T * H // 128
+    lane = np.arange(64)
+    for tile in range(ntiles):
+        P0 = tile * TILE
+        eb = find_expert(offc, E, P0)
+        e = eb + lane
+        ok = e < E
+        c_off = np.where(ok, offc[np.minimum(e, E - 1)], T)
+        c_n = np.where(ok, np.maximum(offc[np.minimum(e + 1, E)] - c_off, 0), 0)
+        c_poff = np.where(ok, 16 * ((c_off + 15) // 16 + e), 2**31 - 1)
+        idx = np.zeros(CHUNKS, np.int64)
+        for q in range(CHUNKS):
+            m = c_poff <= P0 + 16 * q
+            idx[q] = np.nonzero(m)[0].max() if m.any() else 0
+        for bp in range(npairs):
+            for wave in range(16):
+                s8 = lane & 7
+                g = 8 * wave + (lane >> 3)
+                q1 = g >> 2
+                i1 = idx[q1]
+                off1, n1 = c_off[i1], c_n[i1]
+                u1 = P0 + 16 * q1 - c_poff[i1] + 4 * (g & 3)
+                b = 2 * bp + (s8 >> 2)
+                for k in range(4):
+                    u = u1 + k
+                    val = (b < HB) & (u >= 0) & (u < n1)
+                    t = off1 + u
+                    a = t * (H // 2) + 128 * bp + 16 * s8
+                    assert np.all(~val | ((a >= 0) & (a + 16 <= code_bytes)))
+                    a = t * (H // 32) + 4 * b
+                    assert np.all(~val | ((a >= 0) & (a + 4 <= scale_bytes)))
+                u = u1 + (s8 & 3)
+                val = (b < HB) & (u >= 0) & (u < n1)
+                a = HB * off1 + b * n1 + u
+                assert np.all(~val | ((a >= 0) & (a < sc_floats)))
+                q2 = lane & 31
+                i2 = idx[q2]
+                off2, n2 = c_off[i2], c_n[i2]
+                u2 = P0 + 16 * q2 - c_poff[i2]
+                blk_ok = 2 * bp + (wave >> 3) < HB
+                L = np.where(blk_ok & (u2 >= 0), np.minimum(np.maximum(n2 - u2, 0), 16), 0)
+                for k in range(8):
+                    h = 256 * bp + 16 * wave + 2 * k + (lane >> 5)
+                    a = H * off2 + u2 + h * n2
+                    assert np.all((L == 0) | ((a >= 0) & (a + L <= out_bytes)))
+
+
+MALFORMED = [
+    [0, 50, 20, 90, 90],                    # a descending step
+    [0, 300, 1000, 40, 600],                # beyond T, then back
+    [-30, 10, 10, 600, 5000],               # negative first offset, last beyond T
+    [400, 100, 0, 600],                     # off[0] != 0, descending
+]
+
+
+@pytest.mark.parametrize("off", MALFORMED + [[0, 3, 3, 200, 513, 600]])
+@pytest.mark.parametrize("H", [128, 384])
+def test_accesses_stay_in_bounds(off, H):
+    check_bounds(np.array(off, np.int64), 600, H)
+
+
+def test_many_experts_and_seams():
+    rng = np.random.default_rng(1)
+    counts = rng.integers(0, 9, size=300)
+    off = np.concatenate([[0], np.cumsum(counts)])
+    check_bounds(off, int(off[-1]), 256)
+    off2 = off.copy()
+    rng.shuffle(off2[1:-1])                 # non-monotone interior
+    check_bounds(off2, int(off[-1]), 256)

@@ -140,3 +140,21 @@ def test_tile_seams(counts, H):
     ro, rs = fp8col.convert(packed, sb, off, H)
     np.testing.assert_array_equal(o, ro)
     np.testing.assert_array_equal(s.view(np.uint32), rs.view(np.uint32))
+
+
+@pytest.mark.parametrize("off", [
+    [0, 50, 20, 90, 90],
+    [0, 300, 1000, 40, 600],
+    [-30, 10, 10, 600, 5000],
+    [400, 100, 0, 600],
+])
+def test_malformed_offsets_stay_in_bounds(off):
+    """Offsets that are not ascending or leave [0, T] are clamped on the
+    device (the header leaves the outputs unspecified): the call completes
+    and nothing is written outside the two output buffers.  The index
+    arithmetic for these inputs is checked on the CPU in
+    test_fp8col_index_model.py."""
+    m = need_gpu()
+    T, H = 600, 384
+    packed, sb = synth.random_mxfp4(T, H, seed=9)
+    convert_gpu(m, packed, sb, np.array(off, np.int64), H)    # guard bands checked inside
