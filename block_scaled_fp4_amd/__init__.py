@@ -100,9 +100,23 @@ def _dev(x):
     return x
 
 
-def _2d(x):
-    rows = x.shape[0] if x.dim() > 1 else 1
-    return rows, x.shape[-1] if x.dim() else 1, x.numel()
+def _arg(t, name, dtype, numel, device, optional=False):
+    """Checks a tensor argument the C ABI only sees as a pointer: same GPU as
+    the main input, contiguous, of `dtype`, with at least `numel` elements
+    (the library writes or reads exactly that many)."""
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, {numel} are needed")
+    return t
 
 
 def fp4_quantize(x, fmt="nvfp4", rounding="rtn", seed=0, step=0, tscale="compute",
@@ -119,6 +133,9 @@ def fp4_quantize(x, fmt="nvfp4", rounding="rtn", seed=0, step=0, tscale="compute
         scales = torch.empty((rows, cols // blk), dtype=torch.uint8, device=x.device)
     if fmt == "nvfp4" and tensor_scale is None:
         tensor_scale = torch.empty(1, dtype=torch.float32, device=x.device)
+    _arg(packed, "packed", torch.uint8, rows * cols // 2, x.device)
+    _arg(scales, "scales", torch.uint8, rows * cols // blk, x.device)
+    _arg(tensor_scale, "tensor_scale", torch.float32, 1, x.device, optional=fmt == "mxfp4")
     _check("fp4_quantize", _lib.fp4_quantize(
         _ptr(x), _dtype_code(x.dtype), rows, cols, FMT[fmt], ROUND[rounding], seed, step,
         TSCALE[tscale], _ptr(tensor_scale), _ptr(packed), _ptr(scales), _stream(stream)))
@@ -131,6 +148,11 @@ def fp4_dequantize(packed, scales, rows, cols, fmt="nvfp4", tensor_scale=None,
     _dev(packed)
     if y is None:
         y = torch.empty((rows, cols), dtype=out_dtype, device=packed.device)
+    blk = 32 if fmt == "mxfp4" else 16
+    _arg(packed, "packed", torch.uint8, rows * cols // 2, packed.device)
+    _arg(scales, "scales", torch.uint8, rows * cols // blk, packed.device)
+    _arg(tensor_scale, "tensor_scale", torch.float32, 1, packed.device, optional=fmt == "mxfp4")
+    _arg(y, "y", y.dtype, rows * cols, packed.device)
     _check("fp4_dequantize", _lib.fp4_dequantize(
         _ptr(packed), _ptr(scales), _ptr(tensor_scale), rows, cols, FMT[fmt], _ptr(y),
         _dtype_code(y.dtype), _stream(stream)))
@@ -149,6 +171,9 @@ def fp4quant_encode(x, group, packed=None, s_rms=None, s_abs=None, stream=None):
         s_rms = torch.empty((rows, ng), dtype=torch.float32, device=x.device)
     if s_abs is None:
         s_abs = torch.empty((rows, ng), dtype=torch.float32, device=x.device)
+    _arg(packed, "packed", torch.uint8, rows * cols // 2, x.device)
+    _arg(s_rms, "s_rms", torch.float32, rows * ng, x.device)
+    _arg(s_abs, "s_abs", torch.float32, rows * ng, x.device)
     _check("fp4quant_encode", _lib.fp4quant_encode(
         _ptr(x), _dtype_code(x.dtype), rows, cols, group, _ptr(packed), _ptr(s_rms), _ptr(s_abs),
         _stream(stream)))
@@ -161,6 +186,11 @@ def fp4quant_decode(packed, s_rms, s_abs, rows, cols, group, out_dtype=torch.bfl
     _dev(packed)
     if y is None:
         y = torch.empty((rows, cols), dtype=out_dtype, device=packed.device)
+    ng = cols // group if group > 0 else 0
+    _arg(packed, "packed", torch.uint8, rows * cols // 2, packed.device)
+    _arg(s_rms, "s_rms", torch.float32, rows * ng, packed.device)
+    _arg(s_abs, "s_abs", torch.float32, rows * ng, packed.device)
+    _arg(y, "y", y.dtype, rows * cols, packed.device)
     _check("fp4quant_decode", _lib.fp4quant_decode(
         _ptr(packed), _ptr(s_rms), _ptr(s_abs), rows, cols, group, _ptr(y), _dtype_code(y.dtype),
         _stream(stream)))
@@ -179,6 +209,12 @@ def fp4_errfeedback_qdq(x, residual=None, y=None, out_dtype=None, rounding="sr",
         y = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
     if tensor_scale is None:
         tensor_scale = torch.empty(1, dtype=torch.float32, device=x.device)
+    n = rows * cols
+    _arg(residual, "residual", torch.float32, n, x.device, optional=True)
+    _arg(y, "y", y.dtype, n, x.device)
+    _arg(tensor_scale, "tensor_scale", torch.float32, 1, x.device)
+    _arg(packed, "packed", torch.uint8, n // 2, x.device, optional=True)
+    _arg(scales, "scales", torch.uint8, n // 16, x.device, optional=True)
     _check("fp4_errfeedback_qdq", _lib.fp4_errfeedback_qdq(
         _ptr(x), _dtype_code(x.dtype), rows, cols, _ptr(residual), _ptr(y), _dtype_code(y.dtype),
         ROUND[rounding], seed, step, TSCALE[tscale], _ptr(tensor_scale), _ptr(packed),
@@ -197,6 +233,11 @@ def mxfp4_row_to_fp8_col(packed, scales_e8m0, token_offsets, hidden, fp8_out=Non
         fp8_out = torch.empty(T * hidden, dtype=torch.uint8, device=packed.device)
     if fp8_scales is None:
         fp8_scales = torch.empty(T * hidden // 128, dtype=torch.float32, device=packed.device)
+    _arg(packed, "packed", torch.uint8, T * hidden // 2, packed.device)
+    _arg(scales_e8m0, "scales_e8m0", torch.uint8, T * hidden // 32, packed.device)
+    _arg(token_offsets, "token_offsets", torch.int64, 1, packed.device)
+    _arg(fp8_out, "fp8_out", torch.uint8, T * hidden, packed.device)
+    _arg(fp8_scales, "fp8_scales", torch.float32, T * hidden // 128, packed.device)
     _check("mxfp4_row_to_fp8_col", _lib.mxfp4_row_to_fp8_col(
         _ptr(packed), _ptr(scales_e8m0), _ptr(token_offsets), E, T, hidden, _ptr(fp8_out),
         _ptr(fp8_scales), _stream(stream)))
@@ -213,6 +254,10 @@ def mxfp4_row_to_fp8_row(packed, scales_e8m0, hidden, fp8_out=None, fp8_scales=N
         fp8_out = torch.empty((T, hidden), dtype=torch.uint8, device=packed.device)
     if fp8_scales is None:
         fp8_scales = torch.empty((T, hidden // 128), dtype=torch.float32, device=packed.device)
+    _arg(packed, "packed", torch.uint8, T * hidden // 2, packed.device)
+    _arg(scales_e8m0, "scales_e8m0", torch.uint8, T * hidden // 32, packed.device)
+    _arg(fp8_out, "fp8_out", torch.uint8, T * hidden, packed.device)
+    _arg(fp8_scales, "fp8_scales", torch.float32, T * hidden // 128, packed.device)
     _check("mxfp4_row_to_fp8_row", _lib.mxfp4_row_to_fp8_row(
         _ptr(packed), _ptr(scales_e8m0), T, hidden, _ptr(fp8_out), _ptr(fp8_scales),
         _stream(stream)))

@@ -132,3 +132,25 @@ def test_random_fp8_row_and_column(E, H, seed):
     qo, qs = fp8col.convert_rows(packed, sb, H)
     np.testing.assert_array_equal(host(r), qo)
     np.testing.assert_array_equal(host(rsc).view(np.uint32), qs.view(np.uint32))
+
+
+def test_binding_checks_tensor_arguments():
+    """The C ABI sees plain pointers, so the binding checks every tensor it
+    passes: an output that is too small, of the wrong dtype, strided or on
+    the host is refused before anything is launched."""
+    m = need_gpu()
+    x = torch.zeros((64, 256), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        m.fp4_quantize(x, "mxfp4", packed=torch.empty((64, 100), dtype=torch.uint8, device="cuda"))
+    with pytest.raises(TypeError):
+        m.fp4_quantize(x, "mxfp4", scales=torch.empty((64, 8), dtype=torch.int32, device="cuda"))
+    with pytest.raises(ValueError):
+        m.fp4_quantize(x, "mxfp4", packed=torch.empty((128, 128), dtype=torch.uint8, device="cuda")[::2])
+    with pytest.raises(ValueError):
+        m.fp4_quantize(x, "nvfp4", tensor_scale=torch.empty(1, dtype=torch.float32))
+    p, s, _ = m.fp4_quantize(x, "mxfp4")
+    with pytest.raises(ValueError):
+        m.fp4_dequantize(p, s, 64, 256, "mxfp4", y=torch.empty((64, 255), dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(ValueError):
+        m.mxfp4_row_to_fp8_row(p, s, 256, fp8_out=torch.empty((64, 128), dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
