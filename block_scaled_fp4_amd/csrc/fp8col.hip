@@ -179,8 +179,9 @@ __device__ int find_expert_t(const int64_t* off, const int* offs, int E, int T, 
   return lo;
 }
 
-// Plan of item (tile, bp): candidate experts e_base + lane, then per chunk
-// the last candidate starting at or before it.
+// Plan of item (tile, bp): candidate experts e_base + lane (e_base starts at
+// or before the tile), then per chunk the last candidate starting at or
+// before it.
 template <bool LDS_TABLE>
 __device__ __forceinline__ ColPlan plan_item(const int64_t* off, const int* offs, int E, int T,
                                              int tile, int bp, int lane, int q1, int g, int q2) {
@@ -193,13 +194,16 @@ __device__ __forceinline__ ColPlan plan_item(const int64_t* off, const int* offs
     c_n = max(off_at<LDS_TABLE>(off, offs, T, e + 1) - c_off, 0);
     c_poff = 16 * ((c_off + 15) / 16 + e);
   }
+  // per lane, the last candidate starting at or before each of its two chunks:
+  // a binary search over the candidates' starts (ascending for ascending
+  // offsets; any other order still yields a candidate index in 0..63)
+  const int t1 = P0 + 16 * q1, t2 = P0 + 16 * q2;
   int i1 = 0, i2 = 0;
 #pragma unroll
-  for (int q = 0; q < kCTile / 16; ++q) {
-    const uint64_t m = __ballot(c_poff <= P0 + 16 * q);
-    const int idx = m ? 63 - __builtin_clzll(m) : 0;
-    i1 = (q == q1) ? idx : i1;
-    i2 = (q == q2) ? idx : i2;
+  for (int st = 32; st >= 1; st >>= 1) {
+    const int a1 = __shfl(c_poff, i1 + st), a2 = __shfl(c_poff, i2 + st);
+    i1 = (a1 <= t1) ? i1 + st : i1;
+    i2 = (a2 <= t2) ? i2 + st : i2;
   }
   ColPlan p;
   p.bp = bp;

@@ -3,8 +3,8 @@ candidate experts, per-lane plans, load and store ranges), run on
 well-formed and malformed token offsets: every load of codes and scales and
 every store of FP8 bytes and fp32 scales must stay inside its buffer.  The
 model follows the kernel's integer steps: padded starts 16 (ceil(off / 16) +
-e) of clamped offsets, a 64-way search per tile, 64 candidate experts, the
-last candidate at or before each 16-position chunk."""
+e) of clamped offsets, a 64-way search per tile, 64 candidate experts, a
+binary search for the last candidate at or before each 16-position chunk."""
 import numpy as np
 import pytest
 
@@ -51,10 +51,12 @@ def check_bounds(off, T, H):
         c_off = np.where(ok, offc[np.minimum(e, E - 1)], T)
         c_n = np.where(ok, np.maximum(offc[np.minimum(e + 1, E)] - c_off, 0), 0)
         c_poff = np.where(ok, 16 * ((c_off + 15) // 16 + e), 2**31 - 1)
-        idx = np.zeros(CHUNKS, np.int64)
+        idx = np.zeros(CHUNKS, np.int64)          # binary search over the 64 candidates
         for q in range(CHUNKS):
-            m = c_poff <= P0 + 16 * q
-            idx[q] = np.nonzero(m)[0].max() if m.any() else 0
+            i, thr = 0, P0 + 16 * q
+            for st in (32, 16, 8, 4, 2, 1):
+                i = i + st if c_poff[i + st] <= thr else i
+            idx[q] = i
         for bp in range(npairs):
             for wave in range(16):
                 s8 = lane & 7
