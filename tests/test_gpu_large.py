@@ -70,3 +70,46 @@ def test_nvfp4_sr_counters_past_2_34_elements():
     rp, rs = nvfp4.quantize_packed(xs, st, "sr", seed=seed, step=step, row_ids=ids)
     np.testing.assert_array_equal(host(s[torch.tensor(ids, device="cuda")]), rs)
     np.testing.assert_array_equal(host(p[torch.tensor(ids, device="cuda")]), rp)
+
+
+def test_fp8_rows_and_columns_past_2_32_output_bytes():
+    """655,360 tokens x 7168 in 256 Zipf(1.1) experts: 4.7 GB of FP8 output,
+    so the late experts' rows sit past byte 2^32."""
+    import synth
+    from oracle import fp8col
+    m = need_gpu()
+    T, H, E = 655360, 7168, 256
+    _need_memory(T * H * (0.5 + 1 / 32 + 2 + 2 / 32))
+    counts, off = synth.expert_counts(T, E, seed=7)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    packed = torch.randint(0, 256, (T, H // 2), generator=g, device="cuda", dtype=torch.uint8)
+    sb = torch.randint(110, 141, (T, H // 32), generator=g, device="cuda", dtype=torch.uint8)
+    off_d = torch.from_numpy(off).cuda()
+    o, s = m.mxfp4_row_to_fp8_col(packed, sb, off_d, H)
+    orow, srow = m.mxfp4_row_to_fp8_row(packed, sb, H)
+    torch.cuda.synchronize()
+    HB = H // 128
+    assert H * int(off[E - 4]) > (1 << 32)
+    for e in (0, E // 2, E - 4, E - 2, E - 1):
+        a, b = int(off[e]), int(off[e + 1])
+        n = b - a
+        if n == 0:
+            continue
+        # token windows at the start, middle and end of the expert (the
+        # conversion has no dependence across tokens)
+        wins = sorted({(0, min(n, 512)), (max(0, n // 2 - 256), min(n, n // 2 + 256)), (max(0, n - 512), n)})
+        for t0, t1 in wins:
+            pk, sc = host(packed[a + t0:a + t1]), host(sb[a + t0:a + t1])
+            for blk in (0, HB - 1):
+                cols, scs = slice(blk * 64, blk * 64 + 64), slice(blk * 4, blk * 4 + 4)
+                ro, rs = fp8col.convert(pk[:, cols], sc[:, scs], np.array([0, t1 - t0], np.int64), 128)
+                rows = o[H * a: H * b].view(H, n)[blk * 128: blk * 128 + 128, t0:t1]
+                np.testing.assert_array_equal(host(rows).reshape(-1), ro)
+                gs = s[HB * a: HB * b].view(HB, n)[blk, t0:t1]
+                np.testing.assert_array_equal(host(gs).view(np.uint32), rs.view(np.uint32))
+            k = min(32, t1 - t0)                          # FP8 rows: the window's first tokens
+            qo, qs = fp8col.convert_rows(pk[:k], sc[:k], H)
+            np.testing.assert_array_equal(host(orow[a + t0:a + t0 + k]), qo)
+            np.testing.assert_array_equal(host(srow[a + t0:a + t0 + k]).view(np.uint32),
+                                          qs.view(np.uint32))
