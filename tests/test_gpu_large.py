@@ -113,3 +113,61 @@ def test_fp8_rows_and_columns_past_2_32_output_bytes():
             np.testing.assert_array_equal(host(orow[a + t0:a + t0 + k]), qo)
             np.testing.assert_array_equal(host(srow[a + t0:a + t0 + k]).view(np.uint32),
                                           qs.view(np.uint32))
+
+
+def test_errfeedback_past_2_32_elements():
+    """fp32 x and residual of 2^32 + 98,304 elements each (16 GiB), SR with a
+    given S_t, in one step: W and the new residual of sampled rows, including
+    the last, bit for bit."""
+    m = need_gpu()
+    R, C = (1 << 17) + 3, 1 << 15
+    _need_memory(R * C * (4 + 4 + 2))
+    xb = _fill(R, C, 13)
+    x = xb.float()
+    del xb
+    r = torch.zeros((R, C), dtype=torch.float32, device="cuda")
+    r[R - 1] = 1e-3                                      # a non-zero residual on the last row
+    w = torch.empty((R, C), dtype=torch.bfloat16, device="cuda")
+    st = np.float32(5.0 / 2688)
+    ts = torch.tensor([st], dtype=torch.float32, device="cuda")
+    ids = [0, R // 2, R - 2, R - 1]
+    xs = host(x[torch.tensor(ids, device="cuda")])
+    rs = host(r[torch.tensor(ids, device="cuda")])
+    m.fp4_errfeedback_qdq(x, r, w, None, "sr", 21, 3, "given", ts)
+    torch.cuda.synchronize()
+    oy, orr, _, _, _ = nvfp4.errfeedback_qdq(xs, rs, st, "sr", seed=21, step=3, row_ids=ids)
+    np.testing.assert_array_equal(host_bf16(w[torch.tensor(ids, device="cuda")]), oy)
+    np.testing.assert_array_equal(host(r[torch.tensor(ids, device="cuda")]).view(np.uint32),
+                                  orr.view(np.uint32))
+
+
+def test_fp4quant_past_2_32_elements():
+    """FP4Quant G = 256 over 2^32 + 98,304 bf16 elements: sampled rows of the
+    codes and scales within the transform's tolerance, and their decode (fp32)
+    against the oracle's decode of the same codes."""
+    from oracle import fp4quant as Q
+    m = need_gpu()
+    R, C, G = (1 << 17) + 3, 1 << 15, 256
+    _need_memory(R * C * (2 + 0.5 + 4) + 2 * R * C // G * 4)
+    x = _fill(R, C, 14)
+    p, s1, s2 = m.fp4quant_encode(x, G)
+    y = m.fp4quant_decode(p, s1, s2, R, C, G, torch.float32)
+    torch.cuda.synchronize()
+    ids = [0, R // 2, R - 1]
+    t = torch.tensor(ids, device="cuda")
+    xs = _rows(x, ids)
+    ph, h1, h2 = host(p[t]), host(s1[t]), host(s2[t])
+    rc, r1, r2 = Q.encode(xs, G)
+    codes = F.unpack_codes(ph)
+
+    def pos(c):
+        mag = np.asarray(c).astype(np.int64) & 7
+        return np.where(mag == 0, 0, np.where((np.asarray(c) & 8) != 0, -1, 1) * mag)
+
+    d = np.abs(pos(codes) - pos(rc))
+    assert d.max() <= 1 and np.mean(d > 0) < 1e-4
+    np.testing.assert_allclose(h1, r1, rtol=1e-6, atol=0)
+    np.testing.assert_allclose(h2, r2, rtol=1e-6, atol=0)
+    ref = Q.decode64(codes, h1, h2, G)
+    tol = 1e-6 * np.repeat(np.abs(ref).reshape(-1, G).max(axis=1), G).reshape(ref.shape)
+    assert np.all(np.abs(host(y[t]).astype(np.float64) - ref) <= tol)
