@@ -19,7 +19,7 @@ sample, and a breakdown of the other operations of the codec at their own
 workload shapes.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-breakdown]
-                       [--no-cpu-baseline] [--cpu-seconds S] [--profile-mode {headline,copy}]
+                       [--no-cpu-baseline] [--cpu-seconds S] [--profile-mode {headline,copy,fp8col}]
        python bench.py --summarize-trace DIR --out FILE --command CMD
        python bench.py --summarize-pmc F_HEAD,F_COPY,W_HEAD,W_COPY --out FILE --command CMD
 """
@@ -165,6 +165,25 @@ def copy_probe(args, torch):
         b.copy_(a)
     torch.cuda.synchronize()
     log(f"[bench] profile-mode copy: {args.steps} copies of {nbytes} bytes")
+
+
+def fp8col_probe(args, torch, fp4, synth):
+    """The FP8-column workload of the breakdown (65,536 x 7168 MXFP4 rows in 256
+    Zipf(1.1) experts), converted `steps` times (PMC runs)."""
+    T, H, E = 65536, 7168, 256
+    counts, off = synth.expert_counts(T, E, seed=5)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    act = torch.randn((T, H), generator=g, device="cuda").to(torch.bfloat16)
+    pk, sc, _ = fp4.fp4_quantize(act, "mxfp4", "rtn")
+    del act
+    offd = torch.from_numpy(off).cuda()
+    o8 = torch.empty(T * H, dtype=torch.uint8, device="cuda")
+    s8 = torch.empty(T * H // 128, dtype=torch.float32, device="cuda")
+    for _ in range(args.steps):
+        fp4.mxfp4_row_to_fp8_col(pk, sc, offd, H, o8, s8)
+    torch.cuda.synchronize()
+    log(f"[bench] profile-mode fp8col: {args.steps} conversions")
 
 
 # ------------------------------------------------------------ breakdown
@@ -395,6 +414,35 @@ def summarize_pmc(dirs, out, command):
     print("\n".join(lines))
 
 
+def summarize_pmc_kernel(dirs, out, command, prefix, alg, title):
+    """FETCH_SIZE / WRITE_SIZE runs of a workload and of the 256 MiB copy ->
+    HBM bytes per launch of the kernel whose short name starts with `prefix`,
+    scaled by the copy calibration, against its algorithmic bytes."""
+    import statistics
+    fk, fc, wk, wc = dirs.split(",")
+    copy_bytes = 256 << 20
+
+    def per_kernel(d, ctr):
+        acc = {}
+        for name, v in _rocpd_rows(d, f"select kernel_name, value from counters_collection "
+                                      f"where counter_name = '{ctr}'"):
+            acc.setdefault(_short(name), []).append(v * 1024.0)
+        return {k: statistics.median(v) for k, v in acc.items()}
+
+    kf = copy_bytes / per_kernel(fc, "FETCH_SIZE")["__amd_rocclr_copyBuffer"]
+    kw = copy_bytes / per_kernel(wc, "WRITE_SIZE")["__amd_rocclr_copyBuffer"]
+    fetch, write = per_kernel(fk, "FETCH_SIZE"), per_kernel(wk, "WRITE_SIZE")
+    k = next(n for n in fetch if n.startswith(prefix))
+    fb, wb = fetch[k] * kf, write[k] * kw
+    lines = [f"# rocprofv3 PMC summary: HBM traffic of {title}", f"# command: {command}",
+             f"# copy calibration: FETCH_SIZE x{kf:.4f}, WRITE_SIZE x{kw:.4f} (256 MiB device copy)",
+             f"kernel: {k}", f"fetch_bytes: {fb:.0f}", f"write_bytes: {wb:.0f}",
+             f"hbm_bytes_per_launch: {fb + wb:.0f}", f"algorithmic_bytes_per_launch: {alg}",
+             f"hbm_over_algorithmic: {(fb + wb) / alg:.4f}"]
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -407,9 +455,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum oracle time for the cpu_baseline leg")
-    ap.add_argument("--profile-mode", choices=["headline", "copy"])
+    ap.add_argument("--profile-mode", choices=["headline", "copy", "fp8col"])
     ap.add_argument("--summarize-pmc", help="FETCH_headline,FETCH_copy,WRITE_headline,WRITE_copy dirs")
     ap.add_argument("--summarize-trace", help="rocprofv3 --kernel-trace output dir")
+    ap.add_argument("--summarize-pmc-fp8col", help="FETCH_fp8col,FETCH_copy,WRITE_fp8col,WRITE_copy dirs")
     ap.add_argument("--out")
     ap.add_argument("--command", default="", help="the profiled command, recorded in the summary")
     args = ap.parse_args()
@@ -419,6 +468,12 @@ def main():
         return 0
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.out, args.command)
+        return 0
+    if args.summarize_pmc_fp8col:
+        T, H = 65536, 7168
+        summarize_pmc_kernel(args.summarize_pmc_fp8col, args.out, args.command, "fp8col_tiles_kernel",
+                             T * H // 2 + T * H // 32 + T * H + 4 * (T * H // 128),
+                             "the MXFP4 -> FP8 column kernel (65536x7168, 256 Zipf(1.1) experts)")
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -436,6 +491,9 @@ def main():
         return 1
     if args.profile_mode == "copy":
         copy_probe(args, torch)
+        return 0
+    if args.profile_mode == "fp8col":
+        fp8col_probe(args, torch, fp4, synth)
         return 0
     h = headline(args, torch, fp4, np, synth)
     if args.profile_mode:
