@@ -1,0 +1,96 @@
+"""Every entry point captured in a HIP graph (torch.cuda.CUDAGraph) and
+replayed several times, with eager work and synchronizations between the
+replays: each replay's outputs must equal the eager call's, bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_util import need_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _replay_check(fn, outs, replays=4):
+    """fn() writes into the tensors `outs`; eager result first, then a captured
+    graph replayed `replays` times, the outputs scrambled before each replay."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()                                      # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    junk = torch.empty(1 << 20, device="cuda").uniform_()
+    for k in range(replays):
+        for o in outs:                            # eager work between replays
+            o.view(torch.uint8).fill_(0x5A + k)
+        junk.mul_(1.0001)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, r in zip(outs, ref):
+            assert torch.equal(o.view(torch.uint8), r.view(torch.uint8)), f"replay {k} differs"
+
+
+def test_graphs_of_every_entry_point():
+    m = need_gpu()
+    torch.manual_seed(0)
+    x = (torch.randn((512, 1024), device="cuda") * 3).to(torch.bfloat16)
+    xf = torch.randn((512, 1024), device="cuda")
+    # NVFP4 with the tensor scale computed (three kernels) and given; MXFP4
+    for fmt, tscale in (("nvfp4", "compute"), ("nvfp4", "given"), ("mxfp4", "compute")):
+        blk = 16 if fmt == "nvfp4" else 32
+        p = torch.empty((512, 512), dtype=torch.uint8, device="cuda")
+        s = torch.empty((512, 1024 // blk), dtype=torch.uint8, device="cuda")
+        ts = torch.tensor([1.5e-3], dtype=torch.float32, device="cuda")
+        y = torch.empty((512, 1024), dtype=torch.bfloat16, device="cuda")
+        outs = [p, s, y] + ([ts] if fmt == "nvfp4" and tscale == "compute" else [])
+
+        def fn(fmt=fmt, tscale=tscale, p=p, s=s, ts=ts, y=y):
+            m.fp4_quantize(x, fmt, "sr", seed=7, step=3, tscale=tscale,
+                           tensor_scale=ts if fmt == "nvfp4" else None, packed=p, scales=s)
+            m.fp4_dequantize(p, s, 512, 1024, fmt, ts if fmt == "nvfp4" else None, y=y)
+        _replay_check(fn, outs)
+    # FP4Quant
+    p = torch.empty((512, 512), dtype=torch.uint8, device="cuda")
+    s1 = torch.empty((512, 16), dtype=torch.float32, device="cuda")
+    s2 = torch.empty((512, 16), dtype=torch.float32, device="cuda")
+    yq = torch.empty((512, 1024), dtype=torch.float32, device="cuda")
+
+    def fq():
+        m.fp4quant_encode(x, 64, p, s1, s2)
+        m.fp4quant_decode(p, s1, s2, 512, 1024, 64, torch.float32, yq)
+    _replay_check(fq, [p, s1, s2, yq])
+    # error feedback (computed scale, the residual restored before each run)
+    r0 = torch.randn((512, 1024), device="cuda") * 1e-3
+    r = r0.clone()
+    w = torch.empty((512, 1024), dtype=torch.bfloat16, device="cuda")
+    ts = torch.empty(1, dtype=torch.float32, device="cuda")
+    pe = torch.empty((512, 512), dtype=torch.uint8, device="cuda")
+    se = torch.empty((512, 64), dtype=torch.uint8, device="cuda")
+
+    def ef():
+        r.copy_(r0)
+        m.fp4_errfeedback_qdq(xf, r, w, None, "sr", 9, 2, "compute", ts, pe, se)
+    _replay_check(ef, [r, w, ts, pe, se])
+    # FP8 rows and columns over ragged experts
+    T, H = 3000, 768
+    counts = np.random.default_rng(3).integers(0, 120, size=40)
+    counts[-1] = T - counts[:-1].sum() if T > counts[:-1].sum() else 0
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    T = int(off[-1])
+    pk, sb = synth.random_mxfp4(T, H, seed=4)
+    pk, sb, offd = torch.from_numpy(pk).cuda(), torch.from_numpy(sb).cuda(), torch.from_numpy(off).cuda()
+    o8 = torch.empty(T * H, dtype=torch.uint8, device="cuda")
+    s8 = torch.empty(T * H // 128, dtype=torch.float32, device="cuda")
+    o8r = torch.empty((T, H), dtype=torch.uint8, device="cuda")
+    s8r = torch.empty((T, H // 128), dtype=torch.float32, device="cuda")
+
+    def f8():
+        m.mxfp4_row_to_fp8_col(pk, sb, offd, H, o8, s8)
+        m.mxfp4_row_to_fp8_row(pk, sb, H, o8r, s8r)
+    _replay_check(f8, [o8, s8, o8r, s8r])
