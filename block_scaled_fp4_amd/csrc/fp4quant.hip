@@ -103,11 +103,26 @@ __device__ __forceinline__ float sumsq(const float (&v)[EPL]) {
 }
 
 // Per-group encode of the EPL elements a lane holds (all lanes of the wave
-// take part: the cross-lane stages need every lane of the group).
+// take part: the cross-lane stages and the ballot need every lane).  A group
+// whose sum of squares leaves [2^-100, 2^126) (tiny, huge or zero groups) is
+// first scaled by a power of two that brings its largest element to [1, 2):
+// codes and s2 do not change under such scaling, s1 is scaled back exactly.
 template <int EPL, int LPG>
 __device__ __forceinline__ void encode_lane(float (&v)[EPL], int lane, float inv_g, float c_s2,
                                             uint32_t (&words)[EPL / 8], float* s1o, float* s2o) {
-  const float ss = group_sum<LPG>(sumsq<EPL>(v));
+  float ss = group_sum<LPG>(sumsq<EPL>(v));
+  int e = 0;
+  const bool odd = !(ss >= 0x1p-100f && ss < 0x1p+126f);
+  if (__builtin_amdgcn_ballot_w64(odd)) {            // rare: some group of the wave
+    float mxx = 0.0f;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) mxx = fmaxf(mxx, fabsf(v[j]));
+    mxx = group_max<LPG>(mxx);
+    e = (odd && mxx > 0.0f) ? __builtin_amdgcn_frexp_expf(mxx) - 1 : 0;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) v[j] = __builtin_amdgcn_ldexpf(v[j], -e);
+    ss = group_sum<LPG>(sumsq<EPL>(v));
+  }
   wht_local<EPL>(v);
   wht_cross<LPG, EPL>(v, lane);
   float mx = 0.0f;
@@ -124,7 +139,7 @@ __device__ __forceinline__ void encode_lane(float (&v)[EPL], int lane, float inv
     for (int j = 0; j < 8; ++j) q[j] = v[8 * k + j] * rq;     // +-0 when zero: code 0 or 8
     words[k] = zero ? 0u : rtn8_unit(q);
   }
-  *s1o = zero ? 0.0f : s1;
+  *s1o = zero ? 0.0f : __builtin_amdgcn_ldexpf(s1, e);
   *s2o = zero ? 0.0f : (mx * c_s2) / s1;
 }
 
@@ -168,6 +183,19 @@ __global__ __launch_bounds__(kThreads) void fp4quant_encode_kernel(
   }
 }
 
+// The receiver's per-group factor s1 s2 / (2 sqrt(G)), formed as
+// s1 * (s2 c_dec).  For the scales the encoder emits (s2 = max|z| / 6 with
+// z of unit RMS, so 1/6 <= s2 <= sqrt(G) / 6) s2 c_dec lies in
+// [1 / (12 sqrt(G)), 1/12] and the product never overflows.  For
+// 0 < s1 < 2^-64 it would lose precision to gradual underflow, so it is
+// returned scaled by 2^64 (*tiny set) and the outputs are scaled back, each
+// rounded once more at the end.
+constexpr int kTinyShift = 64;
+__device__ __forceinline__ float group_factor(float s1, float s2, float c_dec, bool* tiny) {
+  *tiny = s1 > 0.0f && s1 < 0x1p-64f;
+  return (*tiny ? s1 * 0x1p+64f : s1) * (s2 * c_dec);
+}
+
 template <bool BF16OUT, int EPL, int LPG>
 __global__ __launch_bounds__(kThreads) void fp4quant_decode_kernel(
     const uint32_t* __restrict__ packed, const float* __restrict__ s_rms,
@@ -178,6 +206,7 @@ __global__ __launch_bounds__(kThreads) void fp4quant_decode_kernel(
   const int64_t base = (int64_t)blockIdx.x * (kThreads * U) + threadIdx.x;
   uint32_t w[U][OCT];
   float f[U];
+  bool tiny[U];
   // 2 * e2m1 values are integers in [-12, 12]; every partial sum of the
   // transform is an integer below 2^14, so fp32 butterflies on them are exact.
 #pragma unroll
@@ -186,7 +215,8 @@ __global__ __launch_bounds__(kThreads) void fp4quant_decode_kernel(
     const bool ok = t < n_lane;
 #pragma unroll
     for (int o = 0; o < OCT; ++o) w[k][o] = ok ? packed[t * OCT + o] : 0u;
-    f[k] = ok ? (s_rms[t / LPG] * s_abs[t / LPG]) * c_dec : 0.0f;
+    f[k] = ok ? group_factor(s_rms[t / LPG], s_abs[t / LPG], c_dec, &tiny[k]) : 0.0f;
+    tiny[k] = ok && tiny[k];
   }
 #pragma unroll
   for (int k = 0; k < U; ++k) {
@@ -201,12 +231,17 @@ __global__ __launch_bounds__(kThreads) void fp4quant_decode_kernel(
     }
     wht_local<EPL>(c);
     wht_cross<LPG, EPL>(c, lane);
+    const bool any_tiny = __builtin_amdgcn_ballot_w64(tiny[k]) != 0;
     if (t >= n_lane) continue;
 #pragma unroll
     for (int o = 0; o < OCT; ++o) {
       float out[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) out[j] = c[8 * o + j] * f[k];
+      if (any_tiny) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) out[j] = __builtin_amdgcn_ldexpf(out[j], tiny[k] ? -kTinyShift : 0);
+      }
       store8<BF16OUT>(y, t * OCT + o, out);
     }
   }
@@ -545,11 +580,12 @@ __global__ __launch_bounds__(64 * kRowWaves) void fq_decode_rows_kernel(
     for (int k = 0; k < kTileOct / 4 / 64; ++k) lcodes[swz_chunk<1>(64 * k + lane)] = a[k];
   }
   float f[U];
+  bool tiny[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t g = t0 / NO + u * D + gw;
     const int64_t gc = g * NO < n_oct ? g : 0;       // past the end: group 0 (not stored)
-    f[u] = (s_rms[gc] * s_abs[gc]) * c_dec;
+    f[u] = group_factor(s_rms[gc], s_abs[gc], c_dec, &tiny[u]);
   }
   wave_lds_sync();
 
@@ -585,12 +621,17 @@ __global__ __launch_bounds__(64 * kRowWaves) void fq_decode_rows_kernel(
     if constexpr (LPG >= 2) row_stage<C, 0>(c);
     if constexpr (LPG >= 4) row_stage<C, 1>(c);
     // outputs -> LDS, layout L0
+    const bool any_tiny = __builtin_amdgcn_ballot_w64(tiny[u]) != 0;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
       const int ch = (gl * NO + r + LPG * s) * NW;
       float o[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) o[j] = c[s][j] * f[u];
+      if (any_tiny) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] = __builtin_amdgcn_ldexpf(o[j], tiny[u] ? -kTinyShift : 0);
+      }
       if constexpr (BF16OUT) {
         lout[swz_chunk<NO * NW>(ch)] = u32x4{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
                                              pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])};

@@ -64,6 +64,20 @@ def e2m1_rtn(q):
     return (m3 | _signbit_code(q)).astype(np.uint8)
 
 
+# Where RTN changes its decision between adjacent grid magnitudes: the
+# midpoints 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.
+E2M1_MIDPOINTS = (E2M1_MAG[:-1] + E2M1_MAG[1:]) / 2
+
+
+def e2m1_rtn_margin(q):
+    """Distance from |q| to the nearest midpoint of adjacent E2M1 magnitudes,
+    i.e. how far q may move before e2m1_rtn picks another grid magnitude
+    (the sign of a zero aside; magnitudes beyond 5 only ever round to 6, so
+    their margin is |q| - 5 as well).  float64."""
+    a = np.abs(np.asarray(q, dtype=np.float64))
+    return np.abs(a[..., None] - E2M1_MIDPOINTS).min(axis=-1)
+
+
 def e2m1_sr(q, u):
     """Stochastic rounding onto the E2M1 grid.
 

@@ -26,16 +26,10 @@ def hadamard(G):
     return scipy.linalg.hadamard(G).astype(np.float64)
 
 
-def encode(x, G):
-    """x: float32 [R, C] (C % G == 0, G a power of two).
-
-    Per group g (G contiguous elements of a row):
-      s1 = sqrt(mean(x**2))      [reading] no epsilon; s1 == 0 -> zeros
-      y  = x / s1
-      z  = H y / sqrt(G)         [reading] orthonormal "normalized" WHT
-      s2 = max|z| / 6            [reading] absmax-to-6, E2M1's largest value
-      code = E2M1 RTN(z / s2)    [reading] no stochastic rounding here
-    Returns (codes uint8 [R, C], s1 float32 [R, C/G], s2 float32 [R, C/G])."""
+def _ratios(x, G):
+    """The steps of the encoder up to the rounding (see encode); returns
+    (q = z / s2 per element [R, C], s1, s2, zero) with s1, s2, zero per
+    group, all float64."""
     x = np.asarray(x, dtype=np.float32).astype(np.float64)
     R, C = x.shape
     assert C % G == 0
@@ -48,12 +42,37 @@ def encode(x, G):
     z = (y @ H.T) / np.sqrt(G)
     s2 = np.max(np.abs(z), axis=1) / 6.0
     s2_safe = np.where(zero | (s2 == 0), 1.0, s2)
-    codes = F.e2m1_rtn(z / s2_safe[:, None])
-    codes[zero] = 0
+    q = z / s2_safe[:, None]
+    q[zero] = 0.0
     s1 = np.where(zero, 0.0, s1)
     s2 = np.where(zero, 0.0, s2)
+    return q.reshape(R, C), s1, s2, zero
+
+
+def encode(x, G):
+    """x: float32 [R, C] (C % G == 0, G a power of two).
+
+    Per group g (G contiguous elements of a row):
+      s1 = sqrt(mean(x**2))      [reading] no epsilon; s1 == 0 -> zeros
+      y  = x / s1
+      z  = H y / sqrt(G)         [reading] orthonormal "normalized" WHT
+      s2 = max|z| / 6            [reading] absmax-to-6, E2M1's largest value
+      code = E2M1 RTN(z / s2)    [reading] no stochastic rounding here
+    Returns (codes uint8 [R, C], s1 float32 [R, C/G], s2 float32 [R, C/G])."""
+    q, s1, s2, zero = _ratios(x, G)
+    R, C = q.shape
+    codes = F.e2m1_rtn(q).reshape(-1, G)
+    codes[zero] = 0
     return (codes.reshape(R, C), s1.astype(np.float32).reshape(R, C // G),
             s2.astype(np.float32).reshape(R, C // G))
+
+
+def ratios(x, G):
+    """The value each code rounds, z / s2 in float64 (0 in zero groups).  A
+    float32 implementation may round a code differently from the oracle only
+    where this value lies within its arithmetic error of an E2M1 rounding
+    boundary (formats.e2m1_rtn_margin)."""
+    return _ratios(x, G)[0]
 
 
 def decode64(codes, s1, s2, G):

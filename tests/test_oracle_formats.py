@@ -85,6 +85,36 @@ def test_e2m1_rtn_grid_points_map_to_themselves_and_monotone():
     assert np.all(np.diff(c) >= 0)
 
 
+def test_e2m1_rtn_margin_is_distance_to_first_decision_change():
+    """Brute force: from each q, bisect in both directions for the first
+    point where e2m1_rtn picks another signed grid magnitude (+-0 merged);
+    the nearer of the two is the margin."""
+    rng = np.random.default_rng(11)
+    mids = F.E2M1_MIDPOINTS
+    q = np.concatenate([rng.uniform(-6.5, 6.5, 600), F.E2M1_MAG, -F.E2M1_MAG, mids, -mids,
+                        mids + 1e-9, mids - 1e-9, [0.0, -0.0, 6.0, 6.5, -6.5]])
+
+    def decision(v):
+        c = F.e2m1_rtn(v).astype(np.int64)
+        return np.where((c & 8) != 0, -1, 1) * (c & 7)
+
+    d0 = decision(q)
+
+    def first_change(sgn):
+        reach = 8.0
+        far = decision(q + sgn * reach) != d0
+        lo, hi = np.zeros_like(q), np.full_like(q, reach)
+        for _ in range(80):
+            mid = (lo + hi) / 2
+            ch = decision(q + sgn * mid) != d0
+            hi, lo = np.where(ch, mid, hi), np.where(ch, lo, mid)
+        return np.where(far, hi, np.inf)
+
+    brute = np.minimum(first_change(1.0), first_change(-1.0))
+    np.testing.assert_allclose(F.e2m1_rtn_margin(q), brute, rtol=0, atol=1e-12)
+    assert np.all(F.e2m1_rtn_margin(mids) == 0) and np.all(F.e2m1_rtn_margin(F.E2M1_MAG[1:-1]) > 0.2)
+
+
 def test_e2m1_rtn_nan_raises():
     with pytest.raises(ValueError):
         F.e2m1_rtn(np.array([np.nan], dtype=np.float32))

@@ -87,6 +87,24 @@ def test_transform_without_rounding_is_identity():
     np.testing.assert_allclose(y @ H.T @ H.T, y, atol=1e-12)
 
 
+@pytest.mark.parametrize("G", [16, 64, 1024])
+def test_two_hot_group_ratios_closed_form(G):
+    """x = a e_i + b e_j (i != j): z is proportional to a H[:, i] + b H[:, j],
+    whose largest magnitude |a| + |b| is reached on the rows where the two
+    columns agree in sign (half of them), so z / s2 is
+    6 (a H[k, i] + b H[k, j]) / (|a| + |b|) for every k."""
+    rng = np.random.default_rng(G)
+    H = Q.hadamard(G)
+    for _ in range(5):
+        i, j = rng.choice(G, 2, replace=False)
+        a, b = np.float32(rng.standard_normal() * 3), np.float32(rng.standard_normal())
+        x = np.zeros((1, G), np.float32)
+        x[0, i], x[0, j] = a, b
+        want = 6.0 * (float(a) * H[:, i] + float(b) * H[:, j]) / (abs(float(a)) + abs(float(b)))
+        np.testing.assert_allclose(Q.ratios(x, G)[0], want, rtol=0, atol=1e-12)
+        np.testing.assert_array_equal(Q.encode(x, G)[0][0], F.e2m1_rtn(want))
+
+
 def test_zero_group():
     x = np.zeros((2, 128), np.float32)
     x[1, 64:] = 1.0
