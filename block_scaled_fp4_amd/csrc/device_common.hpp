@@ -21,6 +21,10 @@ constexpr int kThreads = 256;
 __device__ __forceinline__ u32x4 ld_u32x4(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
+// A plain (cached) load, for data that a later kernel reads again.
+__device__ __forceinline__ u32x4 ld_u32x4_keep(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
 __device__ __forceinline__ void st_u32x4(void* p, u32x4 v) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }

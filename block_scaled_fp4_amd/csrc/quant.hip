@@ -423,14 +423,14 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_kernel(const void* __restri
       const bool ok = i < n_oct;
       const u32x4 z = {0u, 0u, 0u, 0u};
       if constexpr (BF16) {
-        a[k] = ok ? ld_u32x4(static_cast<const uint8_t*>(x) + i * 16) : z;
+        a[k] = ok ? ld_u32x4_keep(static_cast<const uint8_t*>(x) + i * 16) : z;
       } else {
-        a[k] = ok ? ld_u32x4(static_cast<const uint8_t*>(x) + i * 32) : z;
-        b[k] = ok ? ld_u32x4(static_cast<const uint8_t*>(x) + i * 32 + 16) : z;
+        a[k] = ok ? ld_u32x4_keep(static_cast<const uint8_t*>(x) + i * 32) : z;
+        b[k] = ok ? ld_u32x4_keep(static_cast<const uint8_t*>(x) + i * 32 + 16) : z;
       }
       if constexpr (RES) {
-        c[k] = ok ? ld_u32x4(reinterpret_cast<const uint8_t*>(r) + i * 32) : z;
-        d[k] = ok ? ld_u32x4(reinterpret_cast<const uint8_t*>(r) + i * 32 + 16) : z;
+        c[k] = ok ? ld_u32x4_keep(reinterpret_cast<const uint8_t*>(r) + i * 32) : z;
+        d[k] = ok ? ld_u32x4_keep(reinterpret_cast<const uint8_t*>(r) + i * 32 + 16) : z;
       }
     }
 #pragma unroll
@@ -755,8 +755,11 @@ extern "C" int fp4_errfeedback_qdq(const void* x, int dtype, int64_t rows, int64
   const int64_t n_oct = n / 8;
   if (!grid_fits(n_oct)) return FP4_ESHAPE;
   if (tscale_mode == FP4_TSCALE_COMPUTE) {
-    int rc = launch_tensor_scale(x, bf16, residual, n_oct, tensor_scale, packed,
-                                 packed ? n / 2 : 0, st);
+    // the amax partials go to an output the encode pass only writes: the
+    // packed codes if requested, else y unless y is x
+    void* scratch = packed ? static_cast<void*>(packed) : (in_place ? nullptr : y);
+    const int64_t scratch_bytes = packed ? pb : (in_place ? 0 : yb);
+    int rc = launch_tensor_scale(x, bf16, residual, n_oct, tensor_scale, scratch, scratch_bytes, st);
     if (rc) return rc;
   }
   uint32_t* pk = reinterpret_cast<uint32_t*>(packed);

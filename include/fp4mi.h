@@ -160,7 +160,9 @@ int fp4quant_decode(const uint8_t* packed, const float* s_rms, const float* s_ab
  *                overlap with the inputs
  *  packed,scales optional outputs (NULL to skip), layouts as fp4_quantize
  *  tensor_scale  device fp32, written (COMPUTE) or read (GIVEN); COMPUTE
- *                uses packed (when given) for partial maxima before the codes
+ *                keeps partial maxima in an output before the codes are
+ *                written: packed when given, else y unless y == x (then a
+ *                device atomic on *tensor_scale)
  */
 int fp4_errfeedback_qdq(const void* x, int dtype, int64_t rows, int64_t cols,
                         float* residual, void* y, int out_dtype,

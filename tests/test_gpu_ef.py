@@ -38,7 +38,9 @@ def _ef_run(m, x_host, xdtype, r_dev, step, rounding, seed, out_dtype, tscale="c
 @pytest.mark.parametrize("xdtype,out_dtype", [("bf16", "bf16"), ("f32", "f32"), ("f32", "bf16")])
 def test_ef_ten_steps_small(rounding, xdtype, out_dtype):
     """The in-place NVFP4 weight loop of the workload at 192 x 1024: each step
-    adds fl32(1e-4 g) to the stored weight and runs qdq with the residual."""
+    adds fl32(1e-4 g) to the stored weight and runs qdq with the residual.
+    Even steps also return the codes (the tensor-scale pass keeps its partial
+    maxima in the packed output), odd steps do not (it keeps them in y)."""
     m = need_gpu()
     rows, cols = 192, 1024
     wb = synth.ef_weight(rows, cols, seed=4)
@@ -50,12 +52,14 @@ def test_ef_ten_steps_small(rounding, xdtype, out_dtype):
         x = (w + u).astype(np.float32)
         x_host = synth.to_bf16_bits(x) if xdtype == "bf16" else x
         x32 = F.bf16_bits_to_f32(x_host) if xdtype == "bf16" else x
-        y, ts, p, s = _ef_run(m, x_host, xdtype, r_dev, step, rounding, 4, out_dtype)
+        codes = step % 2 == 0
+        y, ts, p, s = _ef_run(m, x_host, xdtype, r_dev, step, rounding, 4, out_dtype, codes=codes)
         oy, r_ref, op, osc, ost = nvfp4.errfeedback_qdq(x32, r_ref, None, rounding, seed=4, step=step,
                                                        out=out_dtype)
         assert np.float32(ts) == ost, step
-        np.testing.assert_array_equal(s, osc)
-        np.testing.assert_array_equal(p, op)
+        if codes:
+            np.testing.assert_array_equal(s, osc)
+            np.testing.assert_array_equal(p, op)
         if out_dtype == "bf16":
             np.testing.assert_array_equal(y, oy)
             w = F.bf16_bits_to_f32(y)
