@@ -215,33 +215,35 @@ def breakdown(args, torch, fp4, np, synth):
     nb = 2 * n + n // 2 + n // 16 + 4
     add("nvfp4_quantize(rtn,compute)", "256x2048 bf16 weight block", nb,
         timed(lambda k: fp4.fp4_quantize(x, "nvfp4", "rtn", packed=p, scales=s, tensor_scale=ts), iters),
-        "4 launches: zero, amax, finalize, encode")
+        "3 launches: amax, reduction of the partial maxima, encode")
     add("nvfp4_dequantize", "256x2048 bf16 weight block", nb,
         timed(lambda k: fp4.fp4_dequantize(p, s, R, C, "nvfp4", ts, y=y), iters))
 
-    # C1 shape at 8192 x 8192: the NVFP4 bandwidth row
+    # C1 shape at 8192 x 8192: the NVFP4 bandwidth row (4 rotating sets, 690 MB,
+    # so that the 256 MB Infinity Cache cannot serve one call's data to the next)
     R, C = 8192, 8192
     n = R * C
+    NS = 4
     g = torch.Generator(device="cuda").manual_seed(11)
-    xs = [(torch.randn((R, C), generator=g, device="cuda") * 0.02).to(torch.bfloat16) for _ in range(2)]
-    ps = [torch.empty((R, C // 2), dtype=torch.uint8, device="cuda") for _ in range(2)]
-    ss = [torch.empty((R, C // 16), dtype=torch.uint8, device="cuda") for _ in range(2)]
-    ys = [torch.empty((R, C), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    xs = [(torch.randn((R, C), generator=g, device="cuda") * 0.02).to(torch.bfloat16) for _ in range(NS)]
+    ps = [torch.empty((R, C // 2), dtype=torch.uint8, device="cuda") for _ in range(NS)]
+    ss = [torch.empty((R, C // 16), dtype=torch.uint8, device="cuda") for _ in range(NS)]
+    ys = [torch.empty((R, C), dtype=torch.bfloat16, device="cuda") for _ in range(NS)]
     ts = torch.empty(1, dtype=torch.float32, device="cuda")
     nb = 2 * n + n // 2 + n // 16
     fp4.fp4_quantize(xs[0], "nvfp4", "rtn", packed=ps[0], scales=ss[0], tensor_scale=ts)
     add("nvfp4_quantize(rtn,given)", "8192x8192 bf16", nb,
-        timed(lambda k: fp4.fp4_quantize(xs[k % 2], "nvfp4", "rtn", tscale="given", tensor_scale=ts,
-                                         packed=ps[k % 2], scales=ss[k % 2]), iters))
+        timed(lambda k: fp4.fp4_quantize(xs[k % NS], "nvfp4", "rtn", tscale="given", tensor_scale=ts,
+                                         packed=ps[k % NS], scales=ss[k % NS]), iters))
     add("nvfp4_quantize(rtn,compute)", "8192x8192 bf16", nb,
-        timed(lambda k: fp4.fp4_quantize(xs[k % 2], "nvfp4", "rtn", tensor_scale=ts,
-                                         packed=ps[k % 2], scales=ss[k % 2]), iters),
+        timed(lambda k: fp4.fp4_quantize(xs[k % NS], "nvfp4", "rtn", tensor_scale=ts,
+                                         packed=ps[k % NS], scales=ss[k % NS]), iters),
         "includes the amax pass (an extra read of x)")
     add("nvfp4_dequantize", "8192x8192 bf16", nb,
-        timed(lambda k: fp4.fp4_dequantize(ps[k % 2], ss[k % 2], R, C, "nvfp4", ts, y=ys[k % 2]), iters))
+        timed(lambda k: fp4.fp4_dequantize(ps[k % NS], ss[k % NS], R, C, "nvfp4", ts, y=ys[k % NS]), iters))
     add("nvfp4_quantize(sr,given)", "8192x8192 bf16", nb,
-        timed(lambda k: fp4.fp4_quantize(xs[k % 2], "nvfp4", "sr", seed=1, step=k, tscale="given",
-                                         tensor_scale=ts, packed=ps[k % 2], scales=ss[k % 2]), iters))
+        timed(lambda k: fp4.fp4_quantize(xs[k % NS], "nvfp4", "sr", seed=1, step=k, tscale="given",
+                                         tensor_scale=ts, packed=ps[k % NS], scales=ss[k % NS]), iters))
     del xs, ps, ss, ys
 
     # C3: FP4Quant codec on the 8192 x 4096 TP tensor, G = 64 and 256
@@ -295,6 +297,57 @@ def breakdown(args, torch, fp4, np, synth):
     add("mxfp4_row_to_fp8_row", "65536x7168", nb,
         timed(lambda k: fp4.mxfp4_row_to_fp8_row(pk, sc, H, o8r, s8r), max(iters // 2, 5)))
     return out
+
+
+# ---------------------------------------------------------------- sweep
+def size_sweep(args, torch, fp4, np):
+    """MXFP4 quantize and dequantize of bf16 [rows, 7168] over a range of
+    sizes; a least-squares fit of time = bytes / BW + t0 separates the
+    fixed cost of a launch (ramp-up, tail, the end-of-kernel cache write-back)
+    from the streaming bandwidth.  Each size rotates enough buffer sets to
+    exceed 768 MB, so the Infinity Cache cannot serve one call's data to the
+    next."""
+    cols = 7168
+    res = {}
+    pts = {"quantize": [], "dequantize": []}
+    g = torch.Generator(device="cuda").manual_seed(12)
+    for rows in args.sweep_rows:
+        n = rows * cols
+        per_set = 2 * n + n // 2 + n // 32 + 2 * n
+        nsets = max(2, -(-(768 << 20) // per_set))
+        x0 = (torch.randn((rows, cols), generator=g, device="cuda") * 0.5).to(torch.bfloat16)
+        sets = [dict(x=x0 if k == 0 else x0.clone(),
+                     p=torch.empty((rows, cols // 2), dtype=torch.uint8, device="cuda"),
+                     s=torch.empty((rows, cols // 32), dtype=torch.uint8, device="cuda"),
+                     y=torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda")) for k in range(nsets)]
+        reps = max(40, nsets)
+
+        def quant(k):
+            S = sets[k % nsets]
+            fp4.fp4_quantize(S["x"], "mxfp4", "rtn", packed=S["p"], scales=S["s"])
+
+        def dequant(k):
+            S = sets[k % nsets]
+            fp4.fp4_dequantize(S["p"], S["s"], rows, cols, "mxfp4", y=S["y"])
+
+        nb = 2 * n + n // 2 + n // 32
+        for name, fn in (("quantize", quant), ("dequantize", dequant)):
+            ms, _ = graph_time(torch, fn, reps, replays=3)
+            pts[name].append((rows, nb, ms * 1e3))
+        log(f"[bench] sweep {rows:6d} x {cols}: {nsets:3d} sets; quantize {pts['quantize'][-1][2]:8.2f} us; "
+            f"dequantize {pts['dequantize'][-1][2]:8.2f} us")
+        del sets, x0
+    for name, pp in pts.items():
+        b = np.array([q[1] for q in pp], np.float64)
+        t = np.array([q[2] for q in pp], np.float64)
+        A = np.stack([b, np.ones_like(b)], axis=1)
+        (inv_bw, t0), *_ = np.linalg.lstsq(A, t, rcond=None)
+        res[name] = dict(bw_fit_GBps=round(1e-3 / inv_bw, 1), t0_us=round(float(t0), 2),
+                         frac_fit_of_hbm_peak=round(1e-3 / inv_bw / HBM_PEAK_GBS, 4),
+                         points=[[r, int(nb), round(us, 2), round(nb / (us * 1e-6) / 1e9, 1)] for r, nb, us in pp])
+        log(f"[bench] sweep fit {name}: {1e-3 / inv_bw:.0f} GB/s streaming + {t0:.2f} us per launch")
+    res["op"] = f"mxfp4 rtn, bf16 [rows, {cols}]; points are [rows, algorithmic bytes, us, GB/s]"
+    return res
 
 
 # ---------------------------------------------------------- cpu baseline
@@ -453,6 +506,9 @@ def main():
     ap.add_argument("--breakdown-iters", type=int, default=30)
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--sweep-rows", type=lambda v: [int(r) for r in v.split(",")],
+                    default=[128, 256, 512, 1024, 2048, 4096, 8192, 16384, 32768])
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum oracle time for the cpu_baseline leg")
     ap.add_argument("--profile-mode", choices=["headline", "copy", "fp8col"])
@@ -531,6 +587,8 @@ def main():
     }
     if not args.no_breakdown:
         res["breakdown"] = breakdown(args, torch, fp4, np, synth)
+    if not args.no_sweep:
+        res["sweep"] = size_sweep(args, torch, fp4, np)
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle for at least {args.cpu_seconds:.0f} s")
         res["cpu_baseline"] = cpu_baseline(h["xb"], min_seconds=args.cpu_seconds)
