@@ -187,21 +187,72 @@ def fp8col_probe(args, torch, fp4, synth):
 
 
 # ------------------------------------------------------------ breakdown
-def breakdown(args, torch, fp4, np, synth):
+def breakdown(args, torch, fp4, np, synth, deferred):
     out = []
     iters = args.breakdown_iters
+    with_oracle = not args.no_cpu_baseline
+    if with_oracle:
+        sys.path.insert(0, ROOT)
+        from oracle import formats as F
+        from oracle import fp4quant as Q
+        from oracle import fp8col as O8
+        from oracle import nvfp4 as NV
 
     def timed(fn, reps):
         return graph_time(torch, fn, reps, replays=3)[0]
 
-    def add(op, workload, nbytes, ms, note=None):
+    def leg(fn, nbytes, what, *fargs, prep=None, **fkw):
+        """An oracle leg: fn(*fargs, **fkw) -- or fn(*prep()) when a prep
+        function builds the arguments, untimed -- on a host sample worth
+        `nbytes` algorithmic bytes.  Everything is bound now; preparation and
+        timing run after the GPU work."""
+        state = {}
+
+        def call():
+            if prep is not None and "args" not in state:
+                state["args"] = prep()
+            fn(*(state["args"] if prep is not None else fargs), **fkw)
+            return nbytes
+        return (call, what)
+
+    def nv_compute(x):
+        return NV.quantize_packed(x, NV.tensor_scale(x))
+
+    def add(op, workload, nbytes, ms, note=None, oracle=None):
+        """oracle: (callable returning the algorithmic bytes of one call on a
+        host sample, description of the sample), timed single-threaded."""
         gbs = nbytes / (ms * 1e-3) / 1e9
         e = dict(op=op, workload=workload, algorithmic_bytes=nbytes, us=round(ms * 1e3, 2),
                  GBps=round(gbs, 1), frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4))
         if note:
             e["note"] = note
+        if with_oracle and oracle is not None:
+            pending.append((e, oracle))
         out.append(e)
         log(f"[bench] {op:28s} {workload:40s} {ms * 1e3:9.1f} us {gbs:8.1f} GB/s")
+
+    # The oracle legs run after every GPU timing: a GPU left idle for seconds
+    # between timings starts the next one at lowered clocks.
+    pending = []
+
+    def time_oracles():
+        try:
+            from threadpoolctl import threadpool_limits
+            one_thread = threadpool_limits(limits=1)        # numpy's BLAS on one thread
+        except Exception:
+            one_thread = None
+        for e, (fn, what) in pending:
+            try:
+                fn()                                        # preparation, untimed
+                r, calls, dt = oracle_rate(fn, args.oracle_row_seconds)
+                e["oracle_GBps_1core"] = round(r, 6)
+                e["oracle_sample"] = f"{what}, {calls} calls in {dt:.1f} s"
+                log(f"[bench] oracle {e['op']:28s} {r * 1e3:9.2f} MB/s ({e['oracle_sample']})")
+            except Exception as ex:                 # a timing leg must not cost the GPU line
+                e["oracle_GBps_1core"] = None
+                log(f"[bench] oracle timing of {e['op']} failed: {ex}")
+        if one_thread is not None:
+            one_thread.restore_original_limits()
 
     # C1: NVFP4 RTN round trip of a 256 x 2048 bf16 weight block (launch bound)
     xb = synth.weight_block()
@@ -213,11 +264,19 @@ def breakdown(args, torch, fp4, np, synth):
     ts = torch.empty(1, dtype=torch.float32, device="cuda")
     y = torch.empty_like(x)
     nb = 2 * n + n // 2 + n // 16 + 4
+    o_q = o_dq = None
+    if with_oracle:
+        def prep_c1(xb=xb):
+            xw = F.bf16_bits_to_f32(xb)
+            stw = NV.tensor_scale(xw)
+            return NV.quantize_packed(xw, stw) + (stw,)
+        o_q = leg(nv_compute, nb, "the whole 256x2048 block", prep=lambda xb=xb: (F.bf16_bits_to_f32(xb),))
+        o_dq = leg(NV.dequantize, nb, "the whole 256x2048 block", prep=prep_c1)
     add("nvfp4_quantize(rtn,compute)", "256x2048 bf16 weight block", nb,
         timed(lambda k: fp4.fp4_quantize(x, "nvfp4", "rtn", packed=p, scales=s, tensor_scale=ts), iters),
-        "3 launches: amax, reduction of the partial maxima, encode")
+        "3 launches: amax, reduction of the partial maxima, encode", oracle=o_q)
     add("nvfp4_dequantize", "256x2048 bf16 weight block", nb,
-        timed(lambda k: fp4.fp4_dequantize(p, s, R, C, "nvfp4", ts, y=y), iters))
+        timed(lambda k: fp4.fp4_dequantize(p, s, R, C, "nvfp4", ts, y=y), iters), oracle=o_dq)
 
     # C1 shape at 8192 x 8192: the NVFP4 bandwidth row (4 rotating sets, 690 MB,
     # so that the 256 MB Infinity Cache cannot serve one call's data to the next)
@@ -232,18 +291,31 @@ def breakdown(args, torch, fp4, np, synth):
     ts = torch.empty(1, dtype=torch.float32, device="cuda")
     nb = 2 * n + n // 2 + n // 16
     fp4.fp4_quantize(xs[0], "nvfp4", "rtn", packed=ps[0], scales=ss[0], tensor_scale=ts)
+    o_g = o_c = o_d = o_sr = None
+    if with_oracle:
+        m = 64
+        xh = xs[0][:m].float().cpu().numpy()
+        sth = np.float32(ts.cpu().numpy()[0])
+        nbm = nb * m // R
+        o_g = leg(NV.quantize_packed, nbm, f"{m} rows, S_t given", xh, sth)
+        o_c = leg(nv_compute, nbm, f"{m} rows, S_t from the sample", xh)
+        o_d = leg(NV.dequantize, nbm, f"{m} rows",
+                  prep=lambda xh=xh, sth=sth: NV.quantize_packed(xh, sth) + (sth,))
+        o_sr = leg(NV.quantize_packed, nbm // 4, "16 rows", xh[:16], sth, "sr", seed=1, step=3)
     add("nvfp4_quantize(rtn,given)", "8192x8192 bf16", nb,
         timed(lambda k: fp4.fp4_quantize(xs[k % NS], "nvfp4", "rtn", tscale="given", tensor_scale=ts,
-                                         packed=ps[k % NS], scales=ss[k % NS]), iters))
+                                         packed=ps[k % NS], scales=ss[k % NS]), iters), oracle=o_g)
     add("nvfp4_quantize(rtn,compute)", "8192x8192 bf16", nb,
         timed(lambda k: fp4.fp4_quantize(xs[k % NS], "nvfp4", "rtn", tensor_scale=ts,
                                          packed=ps[k % NS], scales=ss[k % NS]), iters),
-        "includes the amax pass (an extra read of x)")
+        "includes the amax pass (an extra read of x)", oracle=o_c)
     add("nvfp4_dequantize", "8192x8192 bf16", nb,
-        timed(lambda k: fp4.fp4_dequantize(ps[k % NS], ss[k % NS], R, C, "nvfp4", ts, y=ys[k % NS]), iters))
+        timed(lambda k: fp4.fp4_dequantize(ps[k % NS], ss[k % NS], R, C, "nvfp4", ts, y=ys[k % NS]), iters),
+        oracle=o_d)
     add("nvfp4_quantize(sr,given)", "8192x8192 bf16", nb,
         timed(lambda k: fp4.fp4_quantize(xs[k % NS], "nvfp4", "sr", seed=1, step=k, tscale="given",
-                                         tensor_scale=ts, packed=ps[k % NS], scales=ss[k % NS]), iters))
+                                         tensor_scale=ts, packed=ps[k % NS], scales=ss[k % NS]), iters),
+        oracle=o_sr)
     del xs, ps, ss, ys
 
     # C3: FP4Quant codec on the 8192 x 4096 TP tensor, G = 64 and 256
@@ -258,11 +330,19 @@ def breakdown(args, torch, fp4, np, synth):
         s2 = [torch.empty((R, C // G), dtype=torch.float32, device="cuda") for _ in range(4)]
         ys = [torch.empty((R, C), dtype=torch.bfloat16, device="cuda") for _ in range(4)]
         nb = 2 * n + n // 2 + 8 * (n // G)
+        o_e = o_de = None
+        if with_oracle:
+            m = 64
+            xq = F.bf16_bits_to_f32(tb[:m])
+            o_e = leg(Q.encode_packed, nb * m // R, f"{m} rows", xq, G)
+            o_de = leg(Q.decode64, nb * m // R, f"{m} rows (float64 output)",
+                       prep=lambda xq=xq, G=G: Q.encode(xq, G) + (G,))
         add(f"fp4quant_encode(G={G})", "8192x4096 bf16 TP tensor", nb,
-            timed(lambda k: fp4.fp4quant_encode(xs[k % 4], G, pk[k % 4], s1[k % 4], s2[k % 4]), iters))
+            timed(lambda k: fp4.fp4quant_encode(xs[k % 4], G, pk[k % 4], s1[k % 4], s2[k % 4]), iters),
+            oracle=o_e)
         add(f"fp4quant_decode(G={G})", "8192x4096 bf16 TP tensor", nb,
             timed(lambda k: fp4.fp4quant_decode(pk[k % 4], s1[k % 4], s2[k % 4], R, C, G, y=ys[k % 4]),
-                  iters))
+                  iters), oracle=o_de)
     del xs, pk, s1, s2, ys, x
 
     # C4: SR + error feedback step on an 8192 x 8192 weight (x fp32, r fp32, W bf16)
@@ -273,11 +353,21 @@ def breakdown(args, torch, fp4, np, synth):
     r = torch.zeros((R, C), dtype=torch.float32, device="cuda")
     ts = torch.empty(1, dtype=torch.float32, device="cuda")
     nb = 4 * n + 4 * n + 4 * n + 2 * n
+    o_ec = o_eg = None
+    if with_oracle:
+        m = 16
+        xe = xf[:m].cpu().numpy()
+        re_ = np.zeros((m, C), np.float32)
+        o_ec = leg(NV.errfeedback_qdq, nb * m // R, f"{m} rows, S_t from the sample", xe, re_, None,
+                   "sr", seed=4, step=1)
+        o_eg = leg(NV.errfeedback_qdq, nb * m // R, f"{m} rows", xe, re_, np.float32(1e-4), "sr",
+                   seed=4, step=1)
     add("errfeedback_qdq(sr,compute)", "8192x8192 fp32 x + fp32 r -> bf16 W", nb,
         timed(lambda k: fp4.fp4_errfeedback_qdq(xf, r, W, None, "sr", 4, k, "compute", ts), max(iters // 2, 5)),
-        "includes the amax pass over x + r (536,870,912 extra bytes read)")
+        "includes the amax pass over x + r (536,870,912 extra bytes read)", oracle=o_ec)
     add("errfeedback_qdq(sr,given)", "8192x8192 fp32 x + fp32 r -> bf16 W", nb,
-        timed(lambda k: fp4.fp4_errfeedback_qdq(xf, r, W, None, "sr", 4, k, "given", ts), max(iters // 2, 5)))
+        timed(lambda k: fp4.fp4_errfeedback_qdq(xf, r, W, None, "sr", 4, k, "given", ts), max(iters // 2, 5)),
+        oracle=o_eg)
     del W, xf, r
 
     # C5: MXFP4 rows -> FP8 columns over 256 Zipf(1.1) expert shards, 65536 x 7168
@@ -290,12 +380,24 @@ def breakdown(args, torch, fp4, np, synth):
     o8 = torch.empty(T * H, dtype=torch.uint8, device="cuda")
     s8 = torch.empty(T * H // 128, dtype=torch.float32, device="cuda")
     nb = T * H // 2 + T * H // 32 + T * H + 4 * (T * H // 128)
+    o_col = o_row = None
+    if with_oracle:
+        m = 512
+        ph8, sh8 = pk[:m].cpu().numpy(), sc[:m].cpu().numpy()
+        offm = np.minimum(off, m).astype(np.int64)             # the experts' tokens among the first m
+        o_col = leg(O8.convert, nb * m // T, f"the first {m} tokens in their expert layout", ph8, sh8,
+                    offm, H)
+        o_row = leg(O8.convert_rows, nb * m // T, f"{m} tokens", ph8, sh8, H)
     add("mxfp4_row_to_fp8_col", "65536x7168, 256 Zipf(1.1) experts", nb,
-        timed(lambda k: fp4.mxfp4_row_to_fp8_col(pk, sc, offd, H, o8, s8), max(iters // 2, 5)))
+        timed(lambda k: fp4.mxfp4_row_to_fp8_col(pk, sc, offd, H, o8, s8), max(iters // 2, 5)),
+        oracle=o_col)
     # the same rows -> FP8 rows (no transpose): the dispatch receiver
     o8r, s8r = o8.view(T, H), s8.view(T, H // 128)
     add("mxfp4_row_to_fp8_row", "65536x7168", nb,
-        timed(lambda k: fp4.mxfp4_row_to_fp8_row(pk, sc, H, o8r, s8r), max(iters // 2, 5)))
+        timed(lambda k: fp4.mxfp4_row_to_fp8_row(pk, sc, H, o8r, s8r), max(iters // 2, 5)),
+        oracle=o_row)
+    del pk, sc, o8, s8, o8r, s8r
+    deferred.append(time_oracles)         # run by the caller once the GPU work is done
     return out
 
 
@@ -351,6 +453,64 @@ def size_sweep(args, torch, fp4, np):
 
 
 # ---------------------------------------------------------- cpu baseline
+def oracle_rate(fn, min_seconds):
+    """GB/s of fn() (which returns the algorithmic bytes of one call), called
+    until at least min_seconds have passed."""
+    nbytes, calls = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        nbytes += fn()
+        calls += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            return nbytes / dt / 1e9, calls, dt
+
+
+def _oracle_roundtrip_chunk(xb_chunk):
+    """Pool worker: the oracle's MXFP4 quantize + dequantize of one chunk of
+    bf16 rows; returns the algorithmic bytes."""
+    if ROOT not in sys.path:
+        sys.path.insert(0, ROOT)
+    from oracle import formats as F
+    from oracle import mxfp4
+    x = F.bf16_bits_to_f32(xb_chunk)
+    p, s = mxfp4.quantize_packed(x)
+    mxfp4.dequantize(p, s, "bf16")
+    n = x.size
+    return 2 * (2 * n + n // 2 + n // 32)
+
+
+def cpu_baseline_pool(xb, procs, rows_chunk=64, min_seconds=10.0):
+    """The same oracle work spread over `procs` worker processes (spawned, one
+    BLAS thread each), passing over the headline input until at least
+    min_seconds have passed."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+    saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+    for k in saved:
+        os.environ[k] = "1"
+    try:
+        chunks = [xb[r0:r0 + rows_chunk] for r0 in range(0, xb.shape[0], rows_chunk)]
+        # an executor (not a Pool): a worker that dies raises instead of being respawned
+        with ProcessPoolExecutor(max_workers=procs, mp_context=mp.get_context("spawn")) as ex:
+            list(ex.map(_oracle_roundtrip_chunk, [c[:1] for c in chunks[:procs]]))  # workers up
+            nbytes, passes = 0, 0
+            t0 = time.perf_counter()
+            while True:
+                nbytes += sum(ex.map(_oracle_roundtrip_chunk, chunks))
+                passes += 1
+                dt = time.perf_counter() - t0
+                if dt >= min_seconds:
+                    break
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    return nbytes / dt / 1e9, passes, dt
+
+
 def cpu_baseline(xb, rows_chunk=512, min_seconds=10.0, max_seconds=30.0):
     """The oracle, untuned, on the host: quantize+dequantize of the headline
     input in chunks of `rows_chunk` rows, passing over the whole tensor until
@@ -375,10 +535,20 @@ def cpu_baseline(xb, rows_chunk=512, min_seconds=10.0, max_seconds=30.0):
         dt = time.perf_counter() - t0
         if dt >= min_seconds or dt > max_seconds:
             break
-    return {"value": round(nbytes / dt / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{rows_done} rows ({rows_done / rows_total:.2f} passes over the "
-                      f"{rows_total}x{xb.shape[1]} input, {rows_chunk}-row chunks), "
-                      f"quantize+dequantize, {dt:.1f} s single-threaded numpy"}
+    one = nbytes / dt / 1e9
+    one_sample = (f"{rows_done} rows ({rows_done / rows_total:.2f} passes over the "
+                  f"{rows_total}x{xb.shape[1]} input, {rows_chunk}-row chunks), {dt:.1f} s")
+    procs = min(16, len(os.sched_getaffinity(0)))
+    try:
+        rate, passes, dtp = cpu_baseline_pool(xb, procs, min_seconds=min_seconds)
+    except Exception as ex:                         # the pooled leg must not cost the GPU line
+        log(f"[bench] pooled oracle failed ({ex}); reporting the single-core leg")
+        return {"value": round(one, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": f"quantize+dequantize of {one_sample}, single-threaded numpy"}
+    return {"value": round(rate, 6), "unit": "GB/s", "cores": procs, "kind": "oracle",
+            "sample": f"quantize+dequantize of the {rows_total}x{xb.shape[1]} input in 64-row chunks "
+                      f"over {procs} worker processes (one thread each), {passes} passes in {dtp:.1f} s",
+            "value_1core": round(one, 6), "sample_1core": one_sample}
 
 
 # ------------------------------------------------------------ PMC summary
@@ -510,7 +680,9 @@ def main():
     ap.add_argument("--sweep-rows", type=lambda v: [int(r) for r in v.split(",")],
                     default=[128, 256, 512, 1024, 2048, 4096, 8192, 16384, 32768])
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="minimum oracle time for the cpu_baseline leg")
+                    help="minimum oracle time for each cpu_baseline leg")
+    ap.add_argument("--oracle-row-seconds", type=float, default=1.0,
+                    help="minimum oracle time per breakdown row")
     ap.add_argument("--profile-mode", choices=["headline", "copy", "fp8col"])
     ap.add_argument("--summarize-pmc", help="FETCH_headline,FETCH_copy,WRITE_headline,WRITE_copy dirs")
     ap.add_argument("--summarize-trace", help="rocprofv3 --kernel-trace output dir")
@@ -585,10 +757,13 @@ def main():
         "roofline": roof,
         "copy_reference_GBps": round(h["copy_GBps"], 1),
     }
+    deferred = []
     if not args.no_breakdown:
-        res["breakdown"] = breakdown(args, torch, fp4, np, synth)
+        res["breakdown"] = breakdown(args, torch, fp4, np, synth, deferred)
     if not args.no_sweep:
         res["sweep"] = size_sweep(args, torch, fp4, np)
+    for fn in deferred:
+        fn()
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle for at least {args.cpu_seconds:.0f} s")
         res["cpu_baseline"] = cpu_baseline(h["xb"], min_seconds=args.cpu_seconds)
