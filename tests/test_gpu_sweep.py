@@ -2,7 +2,9 @@
 random shapes (ragged rows, several block rows), random value mixes (heavy
 tails, exact zeros and negative zeros, tiny and large magnitudes, per-row
 exponent spread) over every format x rounding x input dtype x tensor-scale
-mode.  Bit-exact codes, scales, tensor scale and dequantized values."""
+mode, and inputs over the whole fp32 exponent range for quantize,
+dequantize and error feedback.  Bit-exact codes, scales, tensor scale,
+dequantized values and residuals."""
 import numpy as np
 import pytest
 import torch
@@ -43,6 +45,13 @@ def test_random_quantize_dequantize(fmt, rounding, dtype, tscale, rows, cols, se
     m = need_gpu()
     rng = np.random.default_rng(seed)
     x = _values(rng, rows, cols)
+    sr_seed, step = int(rng.integers(1 << 62)), int(rng.integers(1 << 40))
+    st = np.float32(rng.uniform(1e-3, 10.0)) if tscale == "given" else None
+    _check_quantize_dequantize(m, x, fmt, rounding, dtype, tscale, st, sr_seed, step)
+
+
+def _check_quantize_dequantize(m, x, fmt, rounding, dtype, tscale, st, sr_seed, step):
+    rows, cols = x.shape
     if dtype == "bf16":
         xb = F.f32_to_bf16_bits(x)
         x = F.bf16_bits_to_f32(xb)
@@ -50,9 +59,8 @@ def test_random_quantize_dequantize(fmt, rounding, dtype, tscale, rows, cols, se
     else:
         x_dev = dev_f32(x)
     blk = 16 if fmt == "nvfp4" else 32
-    sr_seed, step = int(rng.integers(1 << 62)), int(rng.integers(1 << 40))
-    if fmt == "nvfp4":
-        st = nvfp4.tensor_scale(x) if tscale == "compute" else np.float32(rng.uniform(1e-3, 10.0))
+    if fmt == "nvfp4" and tscale == "compute":
+        st = nvfp4.tensor_scale(x)
     gp, gs = Guarded(rows * cols // 2), Guarded(rows * cols // blk)
     ts = dev_f32(np.array([0.0 if fmt == "mxfp4" or tscale == "compute" else st], np.float32))
     p, s, ts_out = m.fp4_quantize(x_dev, fmt, rounding, sr_seed, step, tscale,
@@ -88,6 +96,103 @@ def test_random_quantize_dequantize(fmt, rounding, dtype, tscale, rows, cols, se
             np.testing.assert_array_equal(got, ref)
         else:
             np.testing.assert_array_equal(got.view(np.uint32), np.asarray(ref, np.float32).view(np.uint32))
+
+
+def _extreme_values(rng, rows, cols, blk, cap=3.0e38):
+    """Every row at its own binary exponent in [-150, 127], 30% of the blocks
+    shifted by another 2^-30 .. 2^30 (blocks far above and below their row,
+    fp32 subnormals, values near the fp32 maximum), exact and negative zeros."""
+    e = rng.integers(-150, 128, size=(rows, 1))
+    t = np.clip(rng.standard_t(3, size=(rows, cols)), -1.99, 1.99)
+    nb = cols // blk
+    kb = rng.integers(-30, 31, size=(rows, nb)) * (rng.random((rows, nb)) < 0.3)
+    x = t * np.exp2(np.clip(e + np.repeat(kb, blk, axis=1), -160, 127).astype(np.float64))
+    r = rng.random((rows, cols))
+    x[r < 0.03] = 0.0
+    x[(r >= 0.03) & (r < 0.04)] = -0.0
+    return np.clip(x, -cap, cap).astype(np.float32)
+
+
+def _extreme_cases():
+    rng = np.random.default_rng(4242)
+    out = []
+    for fmt in ("nvfp4", "mxfp4"):
+        for rounding in ("rtn", "sr"):
+            for dtype in ("bf16", "f32"):
+                for tscale in (("compute", "given") if fmt == "nvfp4" else ("compute", "compute")):
+                    out.append((fmt, rounding, dtype, tscale, int(rng.integers(1, 200)),
+                                32 * int(rng.integers(1, 48)), int(rng.integers(1 << 30))))
+    return out
+
+
+@pytest.mark.parametrize("fmt,rounding,dtype,tscale,rows,cols,seed", _extreme_cases())
+def test_extreme_magnitudes_quantize_dequantize(fmt, rounding, dtype, tscale, rows, cols, seed):
+    """Inputs over the whole fp32 exponent range and, for a given S_t, tensor
+    scales from 2^-149 to 2^127.9 (outside the range where the kernels use
+    division-free quotients): still bit-exact."""
+    m = need_gpu()
+    rng = np.random.default_rng(seed)
+    x = _extreme_values(rng, rows, cols, 16 if fmt == "nvfp4" else 32)
+    sr_seed, step = int(rng.integers(1 << 62)), int(rng.integers(1 << 40))
+    st = np.float32(np.exp2(rng.uniform(-149, 127.9))) if tscale == "given" else None
+    _check_quantize_dequantize(m, x, fmt, rounding, dtype, tscale, st, sr_seed, step)
+
+
+def _extreme_ef_cases():
+    rng = np.random.default_rng(4343)
+    out = []
+    for rounding in ("rtn", "sr"):
+        for xdt, odt in (("bf16", "bf16"), ("f32", "f32"), ("f32", "bf16"), ("bf16", "f32")):
+            for tscale in ("compute", "given"):
+                out.append((rounding, xdt, odt, tscale, int(rng.integers(1, 150)),
+                            16 * int(rng.integers(1, 64)), int(rng.integers(1 << 30))))
+    return out
+
+
+@pytest.mark.parametrize("rounding,xdt,odt,tscale,rows,cols,seed", _extreme_ef_cases())
+def test_extreme_magnitudes_error_feedback(rounding, xdt, odt, tscale, rows, cols, seed):
+    """Error feedback on the same extreme inputs (|x| <= 1e38 so that x + r
+    stays finite), residuals up to 0.3 |x|, with and without codes: output,
+    residual, codes, scales and S_t bit-exact."""
+    m = need_gpu()
+    rng = np.random.default_rng(seed)
+    x = _extreme_values(rng, rows, cols, 16, cap=1e38)
+    if xdt == "bf16":
+        xb = F.f32_to_bf16_bits(x)
+        x = F.bf16_bits_to_f32(xb)
+        x_dev = dev_bf16(xb)
+    else:
+        x_dev = dev_f32(x)
+    r = (x * rng.uniform(-0.3, 0.3, size=x.shape)).astype(np.float32)
+    v = (x + r).astype(np.float32)
+    assert np.all(np.isfinite(v))
+    st = np.float32(np.exp2(rng.uniform(-149, 127.9))) if tscale == "given" else None
+    sr_seed, step = int(rng.integers(1 << 62)), int(rng.integers(1 << 40))
+    codes = bool(seed & 1)
+    od = torch.bfloat16 if odt == "bf16" else torch.float32
+    gy = Guarded(rows * cols * (2 if odt == "bf16" else 4))
+    y = gy.view(od, (rows, cols))
+    ts = dev_f32(np.array([st if tscale == "given" else 0.0], np.float32))
+    gp = Guarded(rows * cols // 2) if codes else None
+    gs = Guarded(rows * cols // 16) if codes else None
+    r_dev = dev_f32(r)
+    m.fp4_errfeedback_qdq(x_dev, r_dev, y, None, rounding, sr_seed, step, tscale, ts,
+                          gp.view(torch.uint8, (rows, cols // 2)) if codes else None,
+                          gs.view(torch.uint8, (rows, cols // 16)) if codes else None)
+    torch.cuda.synchronize()
+    for g in (gy, gp, gs):
+        if g is not None:
+            g.check()
+    oy, orr, op, osc, ost = nvfp4.errfeedback_qdq(x, r, st, rounding, seed=sr_seed, step=step, out=odt)
+    assert np.float32(host(ts)[0]) == np.float32(ost)
+    if odt == "bf16":
+        np.testing.assert_array_equal(host_bf16(y), oy)
+    else:
+        np.testing.assert_array_equal(host(y).view(np.uint32), np.asarray(oy, np.float32).view(np.uint32))
+    np.testing.assert_array_equal(host(r_dev).view(np.uint32), orr.view(np.uint32))
+    if codes:
+        np.testing.assert_array_equal(host(gs.view(torch.uint8, (rows, cols // 16))), osc)
+        np.testing.assert_array_equal(host(gp.view(torch.uint8, (rows, cols // 2))), op)
 
 
 def _fp8_cases():
