@@ -582,17 +582,25 @@ def _short(name):
 
 
 def summarize_trace(directory, out, command):
-    """rocprofv3 --kernel-trace --stats output -> per-kernel duration table."""
+    """rocprofv3 --kernel-trace --stats output -> a duration table per kernel
+    and launch shape (workgroups x threads), so that launches of one kernel at
+    different sizes are not averaged together."""
     import statistics
-    per = {}
-    for name, dur in _rocpd_rows(directory, "select name, duration from kernels"):
-        per.setdefault(_short(name), []).append(dur / 1e3)
-    lines = [f"# rocprofv3 kernel trace summary (durations in us)", f"# command: {command}",
-             f"# source_digest: {source_digest()}",
-             f"{'kernel':60s} {'calls':>6s} {'mean':>9s} {'median':>9s} {'min':>9s} {'max':>9s}"]
+    per, info = {}, {}
+    for name, dur, gx, wx, vgpr, lds in _rocpd_rows(
+            directory, "select name, duration, grid_x, workgroup_x, vgpr_count, lds_size from kernels"):
+        key = (_short(name), int(gx) // max(int(wx), 1), int(wx))
+        per.setdefault(key, []).append(dur / 1e3)
+        info[key] = (vgpr, lds)
+    lines = [f"# rocprofv3 kernel trace summary (durations in us; one row per kernel and launch shape)",
+             f"# command: {command}", f"# source_digest: {source_digest()}",
+             f"{'kernel':56s} {'workgroups x threads':>22s} {'calls':>6s} {'mean':>9s} {'median':>9s} "
+             f"{'min':>9s} {'max':>9s} {'vgpr':>5s} {'lds':>7s}"]
     for k, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
-        lines.append(f"{k[:60]:60s} {len(v):6d} {statistics.mean(v):9.2f} {statistics.median(v):9.2f} "
-                     f"{min(v):9.2f} {max(v):9.2f}")
+        shape = f"{k[1]} x {k[2]}"
+        vg, ld = info[k]
+        lines.append(f"{k[0][:56]:56s} {shape:>22s} {len(v):6d} {statistics.mean(v):9.2f} "
+                     f"{statistics.median(v):9.2f} {min(v):9.2f} {max(v):9.2f} {vg:>5} {ld:>7}")
     open(out, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
