@@ -9,6 +9,28 @@ if ROOT not in sys.path:
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
+# Mutation testing of the oracle's pins (tests/test_oracle_mutants.py): when
+# FP4_ORACLE_MUTATION holds a JSON [module, text, replacement], that oracle
+# module is loaded from its source with the one replacement before any test
+# imports the oracle, so the CPU pins run against a deliberately wrong oracle.
+_MUTATION = os.environ.get("FP4_ORACLE_MUTATION")
+if _MUTATION:
+    import importlib
+    import importlib.util
+    import json
+
+    _mod, _old, _new = json.loads(_MUTATION)
+    importlib.import_module("oracle")
+    _spec = importlib.util.find_spec(_mod)
+    with open(_spec.origin) as _f:
+        _src = _f.read()
+    if _src.count(_old) != 1:
+        raise RuntimeError(f"mutation text does not occur exactly once in {_mod}")
+    _m = importlib.util.module_from_spec(_spec)
+    sys.modules[_mod] = _m
+    exec(compile(_src.replace(_old, _new), _spec.origin, "exec"), _m.__dict__)
+    setattr(sys.modules["oracle"], _mod.rsplit(".", 1)[1], _m)
+
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")

@@ -91,3 +91,17 @@ def test_sr_is_unbiased_at_power_of_two_scale():
     v = F.e2m1_decode(codes[:, 1:])
     assert set(np.unique(v)) == {2.0, 3.0}
     assert abs(v.mean() - 2.3) < 4 * np.sqrt(0.21 / v.size)
+
+
+def test_sr_stream_depends_only_on_the_flat_index():
+    """As for NVFP4: the SR draws follow the row-major position of the
+    element, so reshaping the tensor's rows does not change a code."""
+    rng = np.random.default_rng(22)
+    R, C = 6, 128
+    x = (rng.standard_normal((R, C)) * 3).astype(np.float32)
+    c, s = mxfp4.quantize(x, "sr", seed=5, step=9)
+    for shape in ((1, R * C), (R // 2, 2 * C)):
+        c2, s2 = mxfp4.quantize(x.reshape(shape), "sr", seed=5, step=9)
+        np.testing.assert_array_equal(c2.reshape(R, C), c)
+        np.testing.assert_array_equal(s2.reshape(-1), s.reshape(-1))
+    assert not np.array_equal(mxfp4.quantize(x, "sr", seed=5, step=10)[0], c)

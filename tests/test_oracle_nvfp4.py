@@ -127,3 +127,20 @@ def test_sampled_rows_use_global_indices():
     rows = np.array([0, 5, 39])
     part, _ = nvfp4.quantize(x[rows], st, "sr", seed=7, step=3, row_ids=rows)
     np.testing.assert_array_equal(part, full[rows])
+
+
+def test_sr_stream_depends_only_on_the_flat_index():
+    """The SR draws are keyed by (seed, step, global index), the row-major
+    position of the element in the tensor, so the codes of an [R, C] tensor
+    are those of the same data seen as [1, R C] or [R / 2, 2 C]: the row pitch
+    of the index is the row length."""
+    rng = np.random.default_rng(21)
+    R, C = 6, 64
+    x = (rng.standard_normal((R, C)) * 3).astype(np.float32)
+    st = nvfp4.tensor_scale(x)
+    c, s = nvfp4.quantize(x, st, "sr", seed=5, step=9)
+    for shape in ((1, R * C), (R // 2, 2 * C)):
+        c2, s2 = nvfp4.quantize(x.reshape(shape), st, "sr", seed=5, step=9)
+        np.testing.assert_array_equal(c2.reshape(R, C), c)
+        np.testing.assert_array_equal(s2.reshape(-1), s.reshape(-1))
+    assert not np.array_equal(nvfp4.quantize(x, st, "sr", seed=6, step=9)[0], c)
