@@ -143,3 +143,34 @@ def test_fp8_row_validation(lib):
     assert call(sb=A + (1 << 30) + 2) == c["FP4_EALIGN"]
     assert call(out=A + 16) == c["FP4_EOVERLAP"]               # output inside the codes
     assert call(sc=A + (2 << 30) + 64) == c["FP4_EOVERLAP"]    # scales inside the FP8 rows
+
+
+def test_binding_raises_without_the_library(tmp_path):
+    """The product path fails loudly when the HIP library is missing: a copy
+    of the package without libfp4mi.so raises ImportError on import."""
+    import shutil
+    import subprocess
+    import sys
+    pkg = tmp_path / "block_scaled_fp4_amd"
+    pkg.mkdir()
+    shutil.copy(os.path.join(ROOT, "block_scaled_fp4_amd", "__init__.py"), pkg / "__init__.py")
+    p = subprocess.run([sys.executable, "-c", "import block_scaled_fp4_amd"], cwd=tmp_path,
+                       capture_output=True, text=True, timeout=300)
+    assert p.returncode != 0
+    assert "ImportError" in p.stderr and "libfp4mi.so" in p.stderr
+
+
+def test_product_code_never_reaches_the_oracle():
+    """No file of the package imports or includes the oracle: there is no
+    CPU fallback for any entry point."""
+    pkg = os.path.join(ROOT, "block_scaled_fp4_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            path = os.path.join(dirpath, f)
+            if f.endswith(".py"):
+                src = open(path).read()
+                assert not re.search(r"^\s*(from|import)\s+(\.*)oracle\b", src, re.M), path
+                assert "importlib" not in src and "__import__" not in src, path
+            elif f.endswith((".hip", ".hpp", ".h", ".cpp")):
+                src = open(path).read()
+                assert not re.search(r"^\s*#\s*include\s*[<\"][^>\"]*oracle", src, re.M), path
