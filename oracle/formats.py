@@ -78,6 +78,17 @@ def e2m1_rtn_margin(q):
     return np.abs(a[..., None] - E2M1_MIDPOINTS).min(axis=-1)
 
 
+def e2m1_sr_margin(q, u):
+    """Distance from |q| to the nearest point where e2m1_sr(., u) changes its
+    decision for this u: the thresholds g_k + u (g_{k+1} - g_k) between
+    adjacent grid magnitudes g_k < g_{k+1} (at u = 0 the first one is 0,
+    where the sign of a non-zero code flips).  float64."""
+    a = np.abs(np.asarray(q, dtype=np.float64))
+    u = np.asarray(u, dtype=np.float64)
+    thr = E2M1_MAG[:-1] + u[..., None] * (E2M1_MAG[1:] - E2M1_MAG[:-1])
+    return np.abs(a[..., None] - thr).min(axis=-1)
+
+
 def e2m1_sr(q, u):
     """Stochastic rounding onto the E2M1 grid.
 

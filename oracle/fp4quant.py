@@ -19,6 +19,7 @@ import numpy as np
 import scipy.linalg
 
 from . import formats as F
+from .philox import sr_uniform
 
 
 def hadamard(G):
@@ -49,7 +50,7 @@ def _ratios(x, G):
     return q.reshape(R, C), s1, s2, zero
 
 
-def encode(x, G):
+def encode(x, G, rounding="rtn", seed=0, step=0, row_ids=None):
     """x: float32 [R, C] (C % G == 0, G a power of two).
 
     Per group g (G contiguous elements of a row):
@@ -57,11 +58,21 @@ def encode(x, G):
       y  = x / s1
       z  = H y / sqrt(G)         [reading] orthonormal "normalized" WHT
       s2 = max|z| / 6            [reading] absmax-to-6, E2M1's largest value
-      code = E2M1 RTN(z / s2)    [reading] no stochastic rounding here
+      code = E2M1 RTN(z / s2)    the article's rounding
+    rounding="sr" is a variant the article does not describe: "fp4-train"'s
+    stochastic rounding ("How it works") applied to z / s2, the draw of
+    each transformed element keyed by (seed, step, its row-major index in
+    the tensor) exactly as for NVFP4; row_ids names the tensor rows x holds
+    when it is a sample of them.
     Returns (codes uint8 [R, C], s1 float32 [R, C/G], s2 float32 [R, C/G])."""
     q, s1, s2, zero = _ratios(x, G)
     R, C = q.shape
-    codes = F.e2m1_rtn(q).reshape(-1, G)
+    if rounding == "rtn":
+        codes = F.e2m1_rtn(q).reshape(-1, G)
+    else:
+        rows = np.arange(R, dtype=np.int64) if row_ids is None else np.asarray(row_ids, np.int64)
+        index = rows[:, None] * C + np.arange(C, dtype=np.int64)[None, :]
+        codes = F.e2m1_sr(q, sr_uniform(index, seed, step)).reshape(-1, G)
     codes[zero] = 0
     return (codes.reshape(R, C), s1.astype(np.float32).reshape(R, C // G),
             s2.astype(np.float32).reshape(R, C // G))
@@ -85,6 +96,6 @@ def decode64(codes, s1, s2, G):
     return (y * np.asarray(s1, np.float64).reshape(-1, 1)).reshape(R, C)
 
 
-def encode_packed(x, G):
-    codes, s1, s2 = encode(x, G)
+def encode_packed(x, G, rounding="rtn", seed=0, step=0, row_ids=None):
+    codes, s1, s2 = encode(x, G, rounding, seed, step, row_ids)
     return F.pack_codes(codes), s1, s2

@@ -182,3 +182,32 @@ def test_pack_roundtrip_and_nibble_order():
     p = F.pack_codes(c)
     assert p[0] == 0x10 and p[7] == 0xFE
     np.testing.assert_array_equal(F.unpack_codes(p), c)
+
+
+def test_e2m1_sr_margin_is_distance_to_first_decision_change():
+    """Brute force, as for the RTN margin: with u fixed, bisect in both
+    directions for the first point where e2m1_sr picks another signed grid
+    magnitude (+-0 merged)."""
+    rng = np.random.default_rng(12)
+    q = np.concatenate([rng.uniform(-6.5, 6.5, 500), F.E2M1_MAG, -F.E2M1_MAG, [0.0, 0.3, -0.3]])
+    u = np.concatenate([rng.random(500), np.zeros(8), np.full(8, 0.5), [0.0, 0.0, 1 - 2.0 ** -24]])
+    u = np.floor(u * 2 ** 24) * 2.0 ** -24                   # the stream's 24-bit values
+
+    def decision(v):
+        c = F.e2m1_sr(v, u).astype(np.int64)
+        return np.where((c & 8) != 0, -1, 1) * (c & 7)
+
+    d0 = decision(q)
+
+    def first_change(sgn):
+        reach = 8.0
+        far = decision(q + sgn * reach) != d0
+        lo, hi = np.zeros_like(q), np.full_like(q, reach)
+        for _ in range(80):
+            mid = (lo + hi) / 2
+            ch = decision(q + sgn * mid) != d0
+            hi, lo = np.where(ch, mid, hi), np.where(ch, lo, mid)
+        return np.where(far, hi, np.inf)
+
+    brute = np.minimum(first_change(1.0), first_change(-1.0))
+    np.testing.assert_allclose(F.e2m1_sr_margin(q, u), brute, rtol=0, atol=1e-12)

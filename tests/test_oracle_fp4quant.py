@@ -111,3 +111,46 @@ def test_zero_group():
     c, s1, s2 = Q.encode(x, 64)
     assert np.all(c[0] == 0) and s1[0, 0] == 0 and s2[0, 0] == 0
     assert np.all(Q.decode64(c, s1, s2, 64)[0] == 0)
+
+
+def _signed_grid(codes):
+    return F.e2m1_decode(codes)
+
+
+def test_sr_variant_brackets_and_is_unbiased():
+    """Stochastic rounding of z / s2: every code is one of the two grid
+    values around z / s2, and over many steps the codes average to z / s2
+    (the SR draws are uniform, so the rounding is unbiased)."""
+    rng = np.random.default_rng(31)
+    G = 64
+    x = rng.standard_normal((1, 2 * G)).astype(np.float32)
+    q = Q.ratios(x, G)[0]
+    a = np.abs(q)
+    lo_i = np.clip(np.searchsorted(F.E2M1_MAG, a, side="right") - 1, 0, 7)
+    lo = np.sign(q) * F.E2M1_MAG[lo_i]
+    hi = np.sign(q) * F.E2M1_MAG[np.minimum(lo_i + 1, 7)]
+    steps = 1024
+    acc = np.zeros_like(q)
+    for t in range(steps):
+        c = Q.encode(x, G, "sr", seed=3, step=t)[0][0]
+        v = _signed_grid(c)
+        assert np.all((v == lo) | (v == hi) | (np.abs(v) == np.abs(lo)) & (lo == 0))
+        acc += v
+    # the spread of one draw is at most half the widest gap (1), so 6 sigma
+    # of the mean of 1024 draws is 6 / 32
+    assert np.max(np.abs(acc / steps - q)) < 6 / 32
+    assert not np.array_equal(Q.encode(x, G, "sr", seed=3, step=0)[0], Q.encode(x, G)[0])
+
+
+def test_sr_variant_stream_follows_the_flat_index():
+    """Codes of the SR variant do not change when the rows are reshaped
+    (groups stay whole) and a sample of rows with row_ids matches those rows
+    of the whole tensor."""
+    rng = np.random.default_rng(32)
+    R, C, G = 4, 256, 64
+    x = rng.standard_normal((R, C)).astype(np.float32)
+    c = Q.encode(x, G, "sr", seed=9, step=4)[0]
+    c2 = Q.encode(x.reshape(1, R * C), G, "sr", seed=9, step=4)[0]
+    np.testing.assert_array_equal(c2.reshape(R, C), c)
+    rows = np.array([1, 3])
+    np.testing.assert_array_equal(Q.encode(x[rows], G, "sr", seed=9, step=4, row_ids=rows)[0], c[rows])
