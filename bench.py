@@ -343,6 +343,14 @@ def breakdown(args, torch, fp4, np, synth, deferred):
         add(f"fp4quant_decode(G={G})", "8192x4096 bf16 TP tensor", nb,
             timed(lambda k: fp4.fp4quant_decode(pk[k % 4], s1[k % 4], s2[k % 4], R, C, G, y=ys[k % 4]),
                   iters), oracle=o_de)
+        o_sr = None
+        if with_oracle:
+            o_sr = leg(Q.encode_packed, nb * 16 // R, "16 rows", F.bf16_bits_to_f32(tb[:16]), G, "sr",
+                       seed=5, step=2)
+        add(f"fp4quant_encode_sr(G={G})", "8192x4096 bf16 TP tensor", nb,
+            timed(lambda k: fp4.fp4quant_encode_ex(xs[k % 4], G, "sr", 5, k, pk[k % 4], s1[k % 4],
+                                                   s2[k % 4]), iters),
+            "stochastic-rounding variant (Philox draws per element)", oracle=o_sr)
     del xs, pk, s1, s2, ys, x
 
     # C4: SR + error feedback step on an 8192 x 8192 weight (x fp32, r fp32, W bf16)

@@ -39,6 +39,7 @@ _SIGS = {
     "fp4_quantize": [_p, _i, _i64, _i64, _i, _i, _u64, _u64, _i, _p, _p, _p, _p],
     "fp4_dequantize": [_p, _p, _p, _i64, _i64, _i, _p, _i, _p],
     "fp4quant_encode": [_p, _i, _i64, _i64, _i32, _p, _p, _p, _p],
+    "fp4quant_encode_ex": [_p, _i, _i64, _i64, _i32, _i, _u64, _u64, _p, _p, _p, _p],
     "fp4quant_decode": [_p, _p, _p, _i64, _i64, _i32, _p, _i, _p],
     "fp4_errfeedback_qdq": [_p, _i, _i64, _i64, _p, _p, _i, _i, _u64, _u64, _i, _p, _p, _p, _p],
     "mxfp4_row_to_fp8_col": [_p, _p, _p, _i32, _i64, _i64, _p, _p, _p],
@@ -161,6 +162,13 @@ def fp4_dequantize(packed, scales, rows, cols, fmt="nvfp4", tensor_scale=None,
 
 def fp4quant_encode(x, group, packed=None, s_rms=None, s_abs=None, stream=None):
     """FP4Quant encode -> (packed [rows, cols/2], s_rms [rows, cols/G], s_abs [rows, cols/G])."""
+    return fp4quant_encode_ex(x, group, "rtn", 0, 0, packed, s_rms, s_abs, stream, _fn="fp4quant_encode")
+
+
+def fp4quant_encode_ex(x, group, rounding="sr", seed=0, step=0, packed=None, s_rms=None, s_abs=None,
+                       stream=None, _fn="fp4quant_encode_ex"):
+    """FP4Quant encode with RTN or stochastic rounding keyed by (seed, step,
+    element index) -> (packed, s_rms, s_abs) as fp4quant_encode."""
     _dev(x)
     cols = x.shape[-1]
     rows = x.numel() // cols if cols else 0
@@ -174,9 +182,14 @@ def fp4quant_encode(x, group, packed=None, s_rms=None, s_abs=None, stream=None):
     _arg(packed, "packed", torch.uint8, rows * cols // 2, x.device)
     _arg(s_rms, "s_rms", torch.float32, rows * ng, x.device)
     _arg(s_abs, "s_abs", torch.float32, rows * ng, x.device)
-    _check("fp4quant_encode", _lib.fp4quant_encode(
-        _ptr(x), _dtype_code(x.dtype), rows, cols, group, _ptr(packed), _ptr(s_rms), _ptr(s_abs),
-        _stream(stream)))
+    if _fn == "fp4quant_encode":
+        status = _lib.fp4quant_encode(_ptr(x), _dtype_code(x.dtype), rows, cols, group, _ptr(packed),
+                                      _ptr(s_rms), _ptr(s_abs), _stream(stream))
+    else:
+        status = _lib.fp4quant_encode_ex(_ptr(x), _dtype_code(x.dtype), rows, cols, group,
+                                         ROUND.get(rounding, 99), seed, step, _ptr(packed), _ptr(s_rms),
+                                         _ptr(s_abs), _stream(stream))
+    _check(_fn, status)
     return packed, s_rms, s_abs
 
 

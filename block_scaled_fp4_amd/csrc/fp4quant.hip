@@ -102,14 +102,29 @@ __device__ __forceinline__ float sumsq(const float (&v)[EPL]) {
   return t[0];
 }
 
+// Stochastic rounding of eight z / s2 values (|q| <= 6 up to rounding) with
+// the draws of global octet oi of the stream keyed by (seed, step): the
+// rounding rule of the NVFP4 path applied to the transformed elements.
+template <bool WIDE>
+__device__ __forceinline__ uint32_t sr8_octet(const float (&q)[8], int64_t oi, uint64_t seed,
+                                              uint64_t step) {
+  uint32_t u[8];
+  sr_draws8<WIDE>(oi, seed, step, u);
+  uint32_t w = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) w |= (e2m1_sr_mag(fabsf(q[j]), u[j], false) | sign_nibble(q[j])) << (4 * j);
+  return w;
+}
+
 // Per-group encode of the EPL elements a lane holds (all lanes of the wave
 // take part: the cross-lane stages and the ballot need every lane).  A group
 // whose sum of squares leaves [2^-100, 2^126) (tiny, huge or zero groups) is
 // first scaled by a power of two that brings its largest element to [1, 2):
 // codes and s2 do not change under such scaling, s1 is scaled back exactly.
-template <int EPL, int LPG>
+template <int EPL, int LPG, bool SR, bool WIDE>
 __device__ __forceinline__ void encode_lane(float (&v)[EPL], int lane, float inv_g, float c_s2,
-                                            uint32_t (&words)[EPL / 8], float* s1o, float* s2o) {
+                                            uint32_t (&words)[EPL / 8], float* s1o, float* s2o,
+                                            int64_t oct0, uint64_t seed, uint64_t step) {
   float ss = group_sum<LPG>(sumsq<EPL>(v));
   int e = 0;
   const bool odd = !(ss >= 0x1p-100f && ss < 0x1p+126f);
@@ -137,7 +152,8 @@ __device__ __forceinline__ void encode_lane(float (&v)[EPL], int lane, float inv
     float q[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) q[j] = v[8 * k + j] * rq;     // +-0 when zero: code 0 or 8
-    words[k] = zero ? 0u : rtn8_unit(q);
+    if constexpr (SR) words[k] = zero ? 0u : sr8_octet<WIDE>(q, oct0 + k, seed, step);
+    else words[k] = zero ? 0u : rtn8_unit(q);
   }
   *s1o = zero ? 0.0f : __builtin_amdgcn_ldexpf(s1, e);
   *s2o = zero ? 0.0f : (mx * c_s2) / s1;
@@ -145,10 +161,11 @@ __device__ __forceinline__ void encode_lane(float (&v)[EPL], int lane, float inv
 
 // Thread t of workgroup b owns lane-items b*256*U + t + 256*k (k < U); each
 // lane-item is EPL consecutive elements, LPG consecutive lane-items a group.
-template <bool BF16, int EPL, int LPG>
+template <bool BF16, int EPL, int LPG, bool SR, bool WIDE>
 __global__ __launch_bounds__(kThreads) void fp4quant_encode_kernel(
     const void* __restrict__ x, int64_t n_lane, float inv_g, float c_s2,
-    uint32_t* __restrict__ packed, float* __restrict__ s_rms, float* __restrict__ s_abs) {
+    uint32_t* __restrict__ packed, float* __restrict__ s_rms, float* __restrict__ s_abs,
+    uint64_t seed, uint64_t step) {
   constexpr int U = (EPL == 8) ? 2 : 1;
   constexpr int OCT = EPL / 8;
   const int lane = threadIdx.x & 63;
@@ -171,7 +188,7 @@ __global__ __launch_bounds__(kThreads) void fp4quant_encode_kernel(
     const int64_t t = base + (int64_t)k * kThreads;
     uint32_t words[OCT];
     float s1, s2;
-    encode_lane<EPL, LPG>(v[k], lane, inv_g, c_s2, words, &s1, &s2);
+    encode_lane<EPL, LPG, SR, WIDE>(v[k], lane, inv_g, c_s2, words, &s1, &s2, t * OCT, seed, step);
     if (t < n_lane) {
 #pragma unroll
       for (int o = 0; o < OCT; ++o) st_u32(packed + t * OCT + o, words[o]);
@@ -426,10 +443,10 @@ __device__ __forceinline__ void wave_lds_sync() {
 // of squares leaves [2^-100, 2^126) (tiny, huge or zero groups) is first
 // scaled by a power of two that brings its largest element to [1, 2): the
 // codes and s2 do not change under such scaling, s1 is scaled back exactly.
-template <bool BF16, int G>
+template <bool BF16, int G, bool SR, bool WIDE>
 __global__ __launch_bounds__(64 * kRowWaves) void fq_encode_rows_kernel(
     const void* __restrict__ x, int64_t n_oct, uint32_t* __restrict__ packed,
-    float* __restrict__ s_rms, float* __restrict__ s_abs) {
+    float* __restrict__ s_rms, float* __restrict__ s_abs, uint64_t seed, uint64_t step) {
   using C = RowCfg<G>;
   constexpr int LPG = C::LPG, S = C::S, D = 64 / LPG, NO = G / 8;
   constexpr int U = kTileOct / (D * NO);             // groups a lane handles in turn
@@ -505,7 +522,9 @@ __global__ __launch_bounds__(64 * kRowWaves) void fq_encode_rows_kernel(
       float q[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) q[j] = v[s][j] * rq;
-      w[s] = rtn8_unit(q) & keep;
+      // slot s holds octet oct_p(r, s) of the group (layout P)
+      if constexpr (SR) w[s] = sr8_octet<WIDE>(q, g * NO + oct_p<C>(r, s), seed, step) & keep;
+      else w[s] = rtn8_unit(q) & keep;
     }
     // codes -> LDS in runs (layout P); word index = gl * NO + octet
 #pragma unroll
@@ -653,14 +672,14 @@ __global__ __launch_bounds__(64 * kRowWaves) void fq_decode_rows_kernel(
   }
 }
 
-template <bool BF16, int G>
+template <bool BF16, int G, bool SR, bool WIDE>
 void launch_encode_rows(const void* x, int64_t n, uint32_t* pk, float* s1, float* s2,
-                        hipStream_t st) {
+                        uint64_t seed, uint64_t step, hipStream_t st) {
   const int64_t n_oct = n / 8;
   const int64_t waves = (n_oct + kTileOct - 1) / kTileOct;
-  hipLaunchKernelGGL((fq_encode_rows_kernel<BF16, G>),
+  hipLaunchKernelGGL((fq_encode_rows_kernel<BF16, G, SR, WIDE>),
                      dim3((unsigned)((waves + kRowWaves - 1) / kRowWaves)), dim3(64 * kRowWaves), 0,
-                     st, x, n_oct, pk, s1, s2);
+                     st, x, n_oct, pk, s1, s2, seed, step);
 }
 template <bool BF16OUT, int G>
 void launch_decode_rows(const uint32_t* pk, const float* s1, const float* s2, int64_t n, void* y,
@@ -673,28 +692,39 @@ void launch_decode_rows(const uint32_t* pk, const float* s1, const float* s2, in
                      st, pk, s1, s2, n_oct, c_dec, y);
 }
 
-template <bool BF16>
-void launch_encode(int G, const void* x, int64_t n, uint32_t* pk, float* s1, float* s2,
-                   hipStream_t st) {
+template <bool BF16, bool SR, bool WIDE>
+void launch_encode_t(int G, const void* x, int64_t n, uint32_t* pk, float* s1, float* s2,
+                     uint64_t seed, uint64_t step, hipStream_t st) {
   const float inv_g = 1.0f / (float)G;
   const float c_s2 = (float)(1.0 / (6.0 * __builtin_sqrt((double)G)));
 #define FP4MI_ENC(EPL, LPG)                                                                   \
   {                                                                                           \
     int64_t nl = n / EPL;                                                                     \
-    hipLaunchKernelGGL((fp4quant_encode_kernel<BF16, EPL, LPG>),                              \
+    hipLaunchKernelGGL((fp4quant_encode_kernel<BF16, EPL, LPG, SR, WIDE>),                    \
                        dim3((unsigned)blocks_for(nl, EPL == 8 ? 2 : 1)),                      \
-                       dim3(kThreads), 0, st, x, nl, inv_g, c_s2, pk, s1, s2);                 \
+                       dim3(kThreads), 0, st, x, nl, inv_g, c_s2, pk, s1, s2, seed, step);     \
   }
   switch (G) {
-    case 16: launch_encode_rows<BF16, 16>(x, n, pk, s1, s2, st); break;
-    case 32: launch_encode_rows<BF16, 32>(x, n, pk, s1, s2, st); break;
-    case 64: launch_encode_rows<BF16, 64>(x, n, pk, s1, s2, st); break;
-    case 128: launch_encode_rows<BF16, 128>(x, n, pk, s1, s2, st); break;
-    case 256: launch_encode_rows<BF16, 256>(x, n, pk, s1, s2, st); break;
+    case 16: launch_encode_rows<BF16, 16, SR, WIDE>(x, n, pk, s1, s2, seed, step, st); break;
+    case 32: launch_encode_rows<BF16, 32, SR, WIDE>(x, n, pk, s1, s2, seed, step, st); break;
+    case 64: launch_encode_rows<BF16, 64, SR, WIDE>(x, n, pk, s1, s2, seed, step, st); break;
+    case 128: launch_encode_rows<BF16, 128, SR, WIDE>(x, n, pk, s1, s2, seed, step, st); break;
+    case 256: launch_encode_rows<BF16, 256, SR, WIDE>(x, n, pk, s1, s2, seed, step, st); break;
     case 512: FP4MI_ENC(8, 64); break;
     case 1024: FP4MI_ENC(16, 64); break;
   }
 #undef FP4MI_ENC
+}
+
+// SR counters 2 i + 1 of octet i stay below 2^32 when 2 n_oct <= 2^32: their
+// second word is then 0 (the narrow form of the draws).
+template <bool BF16>
+void launch_encode(int G, const void* x, int64_t n, uint32_t* pk, float* s1, float* s2, bool sr,
+                   uint64_t seed, uint64_t step, hipStream_t st) {
+  if (!sr) launch_encode_t<BF16, false, false>(G, x, n, pk, s1, s2, seed, step, st);
+  else if (2 * (n / 8) <= (int64_t(1) << 32))
+    launch_encode_t<BF16, true, false>(G, x, n, pk, s1, s2, seed, step, st);
+  else launch_encode_t<BF16, true, true>(G, x, n, pk, s1, s2, seed, step, st);
 }
 
 template <bool BF16OUT>
@@ -729,9 +759,17 @@ using namespace fp4mi;
 
 extern "C" int fp4quant_encode(const void* x, int dtype, int64_t rows, int64_t cols, int32_t group,
                                uint8_t* packed, float* s_rms, float* s_abs, void* stream) {
+  return fp4quant_encode_ex(x, dtype, rows, cols, group, FP4_ROUND_RTN, 0, 0, packed, s_rms, s_abs,
+                            stream);
+}
+
+extern "C" int fp4quant_encode_ex(const void* x, int dtype, int64_t rows, int64_t cols,
+                                  int32_t group, int rounding, uint64_t seed, uint64_t step,
+                                  uint8_t* packed, float* s_rms, float* s_abs, void* stream) {
   int es = dtype_size(dtype);
   if (!es) return FP4_EDTYPE;
   if (!valid_group(group)) return FP4_EINVAL;
+  if (rounding != FP4_ROUND_RTN && rounding != FP4_ROUND_SR) return FP4_EINVAL;
   int64_t n;
   if (!checked_count(rows, cols, &n)) return FP4_ESHAPE;
   if (cols % group) return FP4_ESHAPE;
@@ -747,8 +785,9 @@ extern "C" int fp4quant_encode(const void* x, int dtype, int64_t rows, int64_t c
   if (blocks_for(n / 8, 1) > 0x7FFFFFFF) return FP4_ESHAPE;
   hipStream_t st = as_stream(stream);
   uint32_t* pk = reinterpret_cast<uint32_t*>(packed);
-  if (dtype == FP4_DTYPE_BF16) launch_encode<true>(group, x, n, pk, s_rms, s_abs, st);
-  else launch_encode<false>(group, x, n, pk, s_rms, s_abs, st);
+  const bool sr = rounding == FP4_ROUND_SR;
+  if (dtype == FP4_DTYPE_BF16) launch_encode<true>(group, x, n, pk, s_rms, s_abs, sr, seed, step, st);
+  else launch_encode<false>(group, x, n, pk, s_rms, s_abs, sr, seed, step, st);
   return launch_status();
 }
 

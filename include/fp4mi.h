@@ -132,6 +132,22 @@ int fp4quant_encode(const void* x, int dtype, int64_t rows, int64_t cols,
                     void* stream);
 
 /*
+ * fp4quant_encode_ex -- fp4quant_encode with a choice of rounding.
+ *
+ * FP4_ROUND_RTN is fp4quant_encode.  FP4_ROUND_SR is a variant the FP4Quant
+ * article does not describe: "fp4-train"'s stochastic rounding (section "How
+ * it works": between two grid points the upper one with probability equal
+ * to the fractional distance) applied to z / s2, the draw of each
+ * transformed element keyed by (seed, step, its row-major index in the
+ * tensor) with the same Philox4x32-10 stream layout as fp4_quantize.  Scales
+ * are those of RTN.  Arguments as fp4quant_encode; rounding outside
+ * {RTN, SR} is FP4_EINVAL.
+ */
+int fp4quant_encode_ex(const void* x, int dtype, int64_t rows, int64_t cols,
+                       int32_t group, int rounding, uint64_t seed, uint64_t step,
+                       uint8_t* packed, float* s_rms, float* s_abs, void* stream);
+
+/*
  * fp4quant_decode -- FP4Quant receiver: unpack, dequantize, inverse WHT
  * (same page, section "Making compression cheap enough to help"):
  *   x' = s1 * H_G (e2m1(code) * s2) / sqrt(G).

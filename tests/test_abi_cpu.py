@@ -96,6 +96,12 @@ def test_other_entry_points_validation(lib):
     assert enc(A, 1, 4, 256, 2048, A + (1 << 30), A + (2 << 30), A + (3 << 30), None) == c["FP4_EINVAL"]
     assert enc(A, 1, 4, 96, 64, A + (1 << 30), A + (2 << 30), A + (3 << 30), None) == c["FP4_ESHAPE"]
     assert enc(A, 1, 4, 256, 64, A + (1 << 30), A + (1 << 30), A + (3 << 30), None) == c["FP4_EOVERLAP"]
+    ex = lib.fp4quant_encode_ex
+    ex.argtypes = [P, I, I64, I64, I32, I, U64, U64, P, P, P, P]
+    assert ex(A, 1, 4, 256, 64, 2, 0, 0, A + (1 << 30), A + (2 << 30), A + (3 << 30), None) == c["FP4_EINVAL"]
+    assert ex(A, 1, 4, 256, 48, 1, 0, 0, A + (1 << 30), A + (2 << 30), A + (3 << 30), None) == c["FP4_EINVAL"]
+    assert ex(A, 1, 4, 96, 64, 1, 0, 0, A + (1 << 30), A + (2 << 30), A + (3 << 30), None) == c["FP4_ESHAPE"]
+    assert ex(A, 1, 0, 256, 64, 1, 0, 0, None, None, None, None) == c["FP4_OK"]
     dec = lib.fp4quant_decode
     dec.argtypes = [P, P, P, I64, I64, I32, P, I, P]
     assert dec(A, A + 4096, A + 8192, 4, 256, 64, A + (1 << 30), 3, None) == c["FP4_EDTYPE"]

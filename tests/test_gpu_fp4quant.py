@@ -17,6 +17,7 @@ import synth
 from gpu_util import Guarded, dev_bf16, dev_f32, host, host_bf16, need_gpu
 from oracle import formats as F
 from oracle import fp4quant as Q
+from oracle.philox import sr_uniform
 
 pytestmark = pytest.mark.gpu
 
@@ -76,6 +77,43 @@ def check_encode(p, s1, s2, x32, G, code_frac=None):
     assert d.max() <= 1
     margin = F.e2m1_rtn_margin(Q.ratios(x32, G))[d > 0]
     assert np.all(margin <= code_tol(G)), (margin.max(), code_tol(G))
+    if code_frac is not None:
+        assert np.mean(d > 0) < code_frac, np.mean(d > 0)
+    np.testing.assert_allclose(s1, r1, rtol=SCALE_RTOL, atol=SUBNORMAL)
+    np.testing.assert_allclose(s2, r2, rtol=s2_rtol(G), atol=0)
+    return codes
+
+
+def encode_gpu_sr(m, x_dev, G, seed, step):
+    rows, cols = x_dev.shape
+    gp, g1, g2 = Guarded(rows * cols // 2), Guarded(rows * cols // G * 4), Guarded(rows * cols // G * 4)
+    p, s1, s2 = m.fp4quant_encode_ex(x_dev, G, "sr", seed, step, gp.view(torch.uint8, (rows, cols // 2)),
+                                     g1.view(torch.float32, (rows, cols // G)),
+                                     g2.view(torch.float32, (rows, cols // G)))
+    torch.cuda.synchronize()
+    for g in (gp, g1, g2):
+        g.check()
+    return host(p), host(s1), host(s2)
+
+
+def check_encode_sr(p, s1, s2, x32, G, seed, step, row_ids=None, code_frac=None):
+    """SR variant: a code may differ from the oracle's only where the oracle's
+    z / s2 lies within the transform's error bound of that element's SR
+    threshold (formats.e2m1_sr_margin with its draw u), by one grid step, or
+    by two where z / s2 itself is that close to 0 (a sign flip at u near 0).
+    Scales as for RTN."""
+    rc, r1, r2 = Q.encode(x32, G, "sr", seed=seed, step=step, row_ids=row_ids)
+    codes = F.unpack_codes(p)
+    d = np.abs(grid_pos(codes) - grid_pos(rc))
+    R, C = x32.shape
+    rows = np.arange(R, dtype=np.int64) if row_ids is None else np.asarray(row_ids, np.int64)
+    u = sr_uniform(rows[:, None] * C + np.arange(C, dtype=np.int64)[None, :], seed, step)
+    q = Q.ratios(x32, G)
+    tol = code_tol(G)
+    assert d.max() <= 2
+    margin = F.e2m1_sr_margin(q, u)[d > 0]
+    assert np.all(margin <= tol), (margin.max(), tol)
+    assert np.all(np.abs(q)[d == 2] <= tol)
     if code_frac is not None:
         assert np.mean(d > 0) < code_frac, np.mean(d > 0)
     np.testing.assert_allclose(s1, r1, rtol=SCALE_RTOL, atol=SUBNORMAL)
@@ -191,3 +229,71 @@ def test_extreme_magnitudes(G, dtype):
     # the decode of the rows whose reconstruction stays inside fp32's range
     keep = np.array([i for i in range(len(x)) if i != k + 2])
     check_decode(m, p[keep], s1[keep], s2[keep], G)
+
+
+@pytest.mark.parametrize("G", [16, 32, 64, 128, 256, 512, 1024])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_sr_variant_all_group_sizes(G, dtype):
+    """fp4quant_encode_ex with stochastic rounding on the edge-case data of
+    test_all_group_sizes_small, two (seed, step) pairs; the RTN entry point
+    and the _ex entry point with RTN give the same bytes."""
+    m = need_gpu()
+    rng = np.random.default_rng(100 + G)
+    rows, cols = 37, 2 * 1024
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    x[:, rng.choice(cols, 20, replace=False)] *= 20
+    x[3] = 0.0
+    x[4, :G] = 0.0
+    x[4, 7] = -2.5
+    x[5, :G] = 0.375
+    x[6] *= 2.0 ** -60
+    x[7] *= 2.0 ** 40
+    if dtype == "bf16":
+        xb = synth.to_bf16_bits(x)
+        x = F.bf16_bits_to_f32(xb)
+        xd = dev_bf16(xb)
+    else:
+        xd = dev_f32(x)
+    for seed, step in ((7, 0), (0x0123456789ABCDEF, (1 << 40) + 3)):
+        p, s1, s2 = encode_gpu_sr(m, xd, G, seed, step)
+        codes = check_encode_sr(p, s1, s2, x, G, seed, step)
+        assert np.all(codes[3] == 0) and np.all(s1[3] == 0)
+    pr, _, _ = encode_gpu(m, xd, G)
+    pe, _, _ = m.fp4quant_encode_ex(xd, G, "rtn")
+    np.testing.assert_array_equal(host(pe), pr)
+
+
+@pytest.mark.parametrize("G", [64, 256, 1024])
+def test_sr_variant_is_unbiased_on_the_gpu(G):
+    """Over 256 steps the GPU's SR codes average to the oracle's z / s2
+    (each draw spreads at most half the widest grid gap, 1: six sigma of a
+    mean of 256 is 6 / 16), while RTN's codes keep their rounding error."""
+    m = need_gpu()
+    rng = np.random.default_rng(200 + G)
+    x = rng.standard_normal((8, 1024)).astype(np.float32)
+    xd = dev_f32(x)
+    q = Q.ratios(x, G)
+    acc = np.zeros_like(q)
+    steps = 256
+    for t in range(steps):
+        p, _, _ = m.fp4quant_encode_ex(xd, G, "sr", 11, t)
+        acc += F.e2m1_decode(F.unpack_codes(host(p)))
+    err = np.abs(acc / steps - q)
+    assert err.max() < 6 / 16
+    rtn = F.e2m1_decode(F.unpack_codes(encode_gpu(m, xd, G)[0]))
+    assert np.mean(err) < 0.5 * np.mean(np.abs(rtn - q))
+
+
+@pytest.mark.parametrize("G", [64, 256])
+def test_sr_variant_tp_tensor_full_size_sampled_rows(G):
+    """8192 x 4096 bf16 TP tensor with stochastic rounding: 32 sampled rows
+    against the oracle run on those rows (row_ids give their stream
+    positions)."""
+    m = need_gpu()
+    xb = synth.tp_tensor()
+    R, C = xb.shape
+    seed, step = 12345, 77
+    p, s1, s2 = encode_gpu_sr(m, dev_bf16(xb), G, seed, step)
+    rows = np.unique(np.concatenate([[0, R - 1], np.random.default_rng(G).choice(R, 30, replace=False)]))
+    check_encode_sr(p[rows], s1[rows], s2[rows], F.bf16_bits_to_f32(xb[rows]), G, seed, step,
+                    row_ids=rows, code_frac=CODE_FRAC)

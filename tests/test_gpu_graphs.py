@@ -65,6 +65,13 @@ def test_graphs_of_every_entry_point():
         m.fp4quant_encode(x, 64, p, s1, s2)
         m.fp4quant_decode(p, s1, s2, 512, 1024, 64, torch.float32, yq)
     _replay_check(fq, [p, s1, s2, yq])
+    # the FP4Quant SR variant (G = 256: the four-lane row layout)
+    s1b = torch.empty((512, 4), dtype=torch.float32, device="cuda")
+    s2b = torch.empty((512, 4), dtype=torch.float32, device="cuda")
+
+    def fqs():
+        m.fp4quant_encode_ex(x, 256, "sr", 5, 8, p, s1b, s2b)
+    _replay_check(fqs, [p, s1b, s2b])
     # error feedback (computed scale, the residual restored before each run)
     r0 = torch.randn((512, 1024), device="cuda") * 1e-3
     r = r0.clone()
@@ -77,6 +84,11 @@ def test_graphs_of_every_entry_point():
         r.copy_(r0)
         m.fp4_errfeedback_qdq(xf, r, w, None, "sr", 9, 2, "compute", ts, pe, se)
     _replay_check(ef, [r, w, ts, pe, se])
+
+    def ef_nocodes():                               # partial maxima kept in w
+        r.copy_(r0)
+        m.fp4_errfeedback_qdq(xf, r, w, None, "sr", 9, 2, "compute", ts)
+    _replay_check(ef_nocodes, [r, w, ts])
     # FP8 rows and columns over ragged experts
     T, H = 3000, 768
     counts = np.random.default_rng(3).integers(0, 120, size=40)

@@ -168,3 +168,21 @@ def test_fp4quant_past_2_32_elements():
     ref = Q.decode64(codes, h1, h2, G)
     tol = 1e-6 * np.repeat(np.abs(ref).reshape(-1, G).max(axis=1), G).reshape(ref.shape)
     assert np.all(np.abs(host(y[t]).astype(np.float64) - ref) <= tol)
+
+
+def test_fp4quant_sr_counters_past_2_34_elements():
+    """The FP4Quant SR variant over 2^34 + 2^21 bf16 elements (G = 256): the
+    draws of the last rows use Philox counters with a non-zero high word.
+    Sampled rows, including the last, within the SR tolerance."""
+    from oracle import fp4quant as Q
+    from test_gpu_fp4quant import check_encode_sr
+    m = need_gpu()
+    R, C, G = (1 << 19) + 64, 1 << 15, 256
+    _need_memory(R * C * (2 + 0.5) + 2 * R * C // G * 4)
+    x = _fill(R, C, 15)
+    seed, step = 0x0123456789ABCDEF, (1 << 33) + 5
+    p, s1, s2 = m.fp4quant_encode_ex(x, G, "sr", seed, step)
+    torch.cuda.synchronize()
+    ids = [0, R // 3, R - 65, R - 64, R - 1]            # the last 64 rows lie past 2^34
+    t = torch.tensor(ids, device="cuda")
+    check_encode_sr(host(p[t]), host(s1[t]), host(s2[t]), _rows(x, ids), G, seed, step, row_ids=ids)
