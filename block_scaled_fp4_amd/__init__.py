@@ -162,13 +162,18 @@ def fp4_dequantize(packed, scales, rows, cols, fmt="nvfp4", tensor_scale=None,
 
 def fp4quant_encode(x, group, packed=None, s_rms=None, s_abs=None, stream=None):
     """FP4Quant encode -> (packed [rows, cols/2], s_rms [rows, cols/G], s_abs [rows, cols/G])."""
-    return fp4quant_encode_ex(x, group, "rtn", 0, 0, packed, s_rms, s_abs, stream, _fn="fp4quant_encode")
+    return _fq_encode("fp4quant_encode", x, group, None, 0, 0, packed, s_rms, s_abs, stream)
 
 
 def fp4quant_encode_ex(x, group, rounding="sr", seed=0, step=0, packed=None, s_rms=None, s_abs=None,
-                       stream=None, _fn="fp4quant_encode_ex"):
+                       stream=None):
     """FP4Quant encode with RTN or stochastic rounding keyed by (seed, step,
     element index) -> (packed, s_rms, s_abs) as fp4quant_encode."""
+    return _fq_encode("fp4quant_encode_ex", x, group, rounding, seed, step, packed, s_rms, s_abs,
+                      stream)
+
+
+def _fq_encode(fn, x, group, rounding, seed, step, packed, s_rms, s_abs, stream):
     _dev(x)
     cols = x.shape[-1]
     rows = x.numel() // cols if cols else 0
@@ -182,14 +187,14 @@ def fp4quant_encode_ex(x, group, rounding="sr", seed=0, step=0, packed=None, s_r
     _arg(packed, "packed", torch.uint8, rows * cols // 2, x.device)
     _arg(s_rms, "s_rms", torch.float32, rows * ng, x.device)
     _arg(s_abs, "s_abs", torch.float32, rows * ng, x.device)
-    if _fn == "fp4quant_encode":
+    if rounding is None:
         status = _lib.fp4quant_encode(_ptr(x), _dtype_code(x.dtype), rows, cols, group, _ptr(packed),
                                       _ptr(s_rms), _ptr(s_abs), _stream(stream))
     else:
         status = _lib.fp4quant_encode_ex(_ptr(x), _dtype_code(x.dtype), rows, cols, group,
                                          ROUND.get(rounding, 99), seed, step, _ptr(packed), _ptr(s_rms),
                                          _ptr(s_abs), _stream(stream))
-    _check(_fn, status)
+    _check(fn, status)
     return packed, s_rms, s_abs
 
 
