@@ -1,6 +1,7 @@
 """Every entry point captured in a HIP graph (torch.cuda.CUDAGraph) and
 replayed several times, with eager work and synchronizations between the
-replays: each replay's outputs must equal the eager call's, bit for bit."""
+replays: each replay's outputs must equal the eager call's, bit for bit.
+And entry points on two streams at once give the bytes of a sequential run."""
 import numpy as np
 import pytest
 import torch
@@ -106,3 +107,40 @@ def test_graphs_of_every_entry_point():
         m.mxfp4_row_to_fp8_col(pk, sb, offd, H, o8, s8)
         m.mxfp4_row_to_fp8_row(pk, sb, H, o8r, s8r)
     _replay_check(f8, [o8, s8, o8r, s8r])
+
+
+def test_two_streams_at_once():
+    """Entry points launched on two non-default streams (default priority)
+    at the same time give the bytes of the same calls run one after another
+    on the default stream: every call keeps to its own buffers and stream."""
+    m = need_gpu()
+    torch.manual_seed(1)
+    x = (torch.randn((2048, 7168), device="cuda") * 2).to(torch.bfloat16)
+    T, H = 4096, 1024
+    counts = np.random.default_rng(8).integers(0, 40, size=128)
+    counts[-1] += T - counts.sum() if T > counts.sum() else 0
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    T = int(off[-1])
+    pk, sb = synth.random_mxfp4(T, H, seed=8)
+    pk, sb, offd = torch.from_numpy(pk).cuda(), torch.from_numpy(sb).cuda(), torch.from_numpy(off).cuda()
+
+    def run(sa, sb_):
+        outs = {}
+        with torch.cuda.stream(sa):
+            p, s, _ = m.fp4_quantize(x, "mxfp4", "rtn", stream=sa)
+            outs["y"] = m.fp4_dequantize(p, s, 2048, 7168, "mxfp4", stream=sa)
+            outs["p"], outs["s"] = p, s
+        with torch.cuda.stream(sb_):
+            outs["o8"], outs["s8"] = m.mxfp4_row_to_fp8_col(pk, sb, offd, H, stream=sb_)
+            outs["o8r"], outs["s8r"] = m.mxfp4_row_to_fp8_row(pk, sb, H, stream=sb_)
+            outs["q"], _, _ = m.fp4quant_encode_ex(x, 256, "sr", 3, 4, stream=sb_)
+        torch.cuda.synchronize()
+        return outs
+
+    d = torch.cuda.current_stream()
+    ref = run(d, d)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for _ in range(3):
+        got = run(s1, s2)
+        for k in ref:
+            assert torch.equal(got[k].view(torch.uint8), ref[k].view(torch.uint8)), k
