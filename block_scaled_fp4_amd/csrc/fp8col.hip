@@ -363,11 +363,16 @@ int launch_fp8col_tiles(const uint8_t* packed, const uint8_t* sb, const int64_t*
 // code bytes sit at 16 s, its block's four UE8M0 bytes are scale dword s / 4
 // (H / 32 is a multiple of 4), its 32 FP8 bytes go to 32 s and its block's
 // fp32 scale to element s / 4 -- every access a plain stream.
-constexpr int kRowItems = 1;                          // sub-blocks per thread (1 measured best)
+constexpr int kRowChunks = 2;                         // 16-channel chunks per thread
 
+// Rows: thread t of workgroup b converts 16-channel chunks c = b 256 K + t +
+// 256 k (k < K) of the flattened [T, H] codes: chunk c is half of the
+// 32-channel sub-block c / 2, its 8 code bytes at 8 c, its 16 FP8 bytes at
+// 16 c.  Every load and store instruction of a wave covers one contiguous
+// range (512 code bytes in, 1 KiB FP8 out).
 __global__ __launch_bounds__(kThreads) void fp8row_kernel(const uint8_t* __restrict__ packed,
                                                          const uint32_t* __restrict__ sb4,
-                                                         int64_t n_sub, uint8_t* __restrict__ out,
+                                                         int64_t n_chunk, uint8_t* __restrict__ out,
                                                          float* __restrict__ sc_out) {
   __shared__ uint32_t lut[(kMaxShift + 1) * 2];
   if (threadIdx.x < (kMaxShift + 1) * 2) {
@@ -376,30 +381,31 @@ __global__ __launch_bounds__(kThreads) void fp8row_kernel(const uint8_t* __restr
     for (int k = 0; k < 4; ++k) w |= remap_e2m1_to_e4m3((uint32_t)(4 * half + k), d) << (8 * k);
     lut[threadIdx.x] = w;
   }
-  const int64_t base = (int64_t)blockIdx.x * (kThreads * kRowItems) + threadIdx.x;
-  u32x4 cw[kRowItems];
-  uint32_t s4[kRowItems];
+  const int64_t base = (int64_t)blockIdx.x * (kThreads * kRowChunks) + threadIdx.x;
+  u32x2 cw[kRowChunks];
+  uint32_t s4[kRowChunks];
 #pragma unroll
-  for (int k = 0; k < kRowItems; ++k) {
-    const int64_t s = base + (int64_t)k * kThreads;
-    const bool ok = s < n_sub;
-    cw[k] = ok ? ld_u32x4(packed + 16 * s) : u32x4{0u, 0u, 0u, 0u};
-    s4[k] = ok ? sb4[s >> 2] : 0u;
+  for (int k = 0; k < kRowChunks; ++k) {
+    const int64_t c = base + (int64_t)k * kThreads;
+    const bool ok = c < n_chunk;
+    cw[k] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(packed + 8 * c))
+               : u32x2{0u, 0u};
+    s4[k] = ok ? sb4[c >> 3] : 0u;
   }
   __syncthreads();
 #pragma unroll
-  for (int k = 0; k < kRowItems; ++k) {
-    const int64_t s = base + (int64_t)k * kThreads;
-    if (s >= n_sub) continue;
+  for (int k = 0; k < kRowChunks; ++k) {
+    const int64_t c = base + (int64_t)k * kThreads;
+    if (c >= n_chunk) continue;
     const uint32_t v4 = s4[k];
     const uint32_t s_tgt = max(max(v4 & 0xFFu, (v4 >> 8) & 0xFFu), max((v4 >> 16) & 0xFFu, v4 >> 24));
-    const uint32_t s_sub = (v4 >> (8 * (s & 3))) & 0xFFu;
+    const uint32_t s_sub = (v4 >> (8 * ((c >> 1) & 3))) & 0xFFu;
     const int d = min((int)(s_tgt - s_sub), kMaxShift);
     const uint32_t tlo = lut[2 * d], thi = lut[2 * d + 1];
-    const uint32_t ww[4] = {cw[k].x, cw[k].y, cw[k].z, cw[k].w};
-    uint32_t o[8];
+    const uint32_t ww[2] = {cw[k].x, cw[k].y};
+    uint32_t o[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 2; ++q) {
       // byte i of ww[q]: channel 8q+2i (low nibble) and 8q+2i+1 (high)
       const uint32_t w = ww[q];
       const uint32_t me = __builtin_amdgcn_perm(thi, tlo, w & 0x07070707u) | ((w << 4) & 0x80808080u);
@@ -407,9 +413,8 @@ __global__ __launch_bounds__(kThreads) void fp8row_kernel(const uint8_t* __restr
       o[2 * q] = __builtin_amdgcn_perm(mo, me, 0x05010400u);       // channels 8q .. 8q+3
       o[2 * q + 1] = __builtin_amdgcn_perm(mo, me, 0x07030602u);   // channels 8q+4 .. 8q+7
     }
-    st_u32x4(out + 32 * s, u32x4{o[0], o[1], o[2], o[3]});
-    st_u32x4(out + 32 * s + 16, u32x4{o[4], o[5], o[6], o[7]});
-    if ((s & 3) == 0) sc_out[s >> 2] = __builtin_amdgcn_ldexpf(1.0f, (int)s_tgt - 127);
+    st_u32x4(out + 16 * c, u32x4{o[0], o[1], o[2], o[3]});
+    if ((c & 7) == 0) sc_out[c >> 3] = __builtin_amdgcn_ldexpf(1.0f, (int)s_tgt - 127);
   }
 }
 
@@ -465,10 +470,11 @@ extern "C" int mxfp4_row_to_fp8_row(const uint8_t* packed, const uint8_t* scales
       overlaps(fp8_out, ob, fp8_scales, scb))
     return FP4_EOVERLAP;
   const int64_t n_sub = n / 32;
-  const int64_t grid = (n_sub + kThreads * kRowItems - 1) / (kThreads * kRowItems);
+  const int64_t n_chunk = 2 * n_sub;
+  const int64_t grid = (n_chunk + kThreads * kRowChunks - 1) / (kThreads * kRowChunks);
   if (grid > 0x7FFFFFFF) return FP4_ESHAPE;
   hipLaunchKernelGGL(fp8row_kernel, dim3((unsigned)grid), dim3(kThreads), 0, as_stream(stream),
-                     packed, reinterpret_cast<const uint32_t*>(scales_e8m0), n_sub, fp8_out,
+                     packed, reinterpret_cast<const uint32_t*>(scales_e8m0), n_chunk, fp8_out,
                      fp8_scales);
   return launch_status();
 }
