@@ -494,7 +494,11 @@ __global__ void tensor_scale_finalize_kernel(float* ts) {
 }
 
 // ------------------------------------------------- error-feedback qdq
-template <bool BF16IN, bool BF16OUT, bool RES, bool SR, bool CODES>
+// KEEP (given S_t): fp32 inputs are read with plain loads.  After the amax
+// pass (computed S_t) they are read with streaming loads, which leave the
+// tail of x and r that the amax pass left in the Infinity Cache in place
+// until this pass reaches it.
+template <bool BF16IN, bool BF16OUT, bool RES, bool SR, bool CODES, bool KEEP>
 __global__ __launch_bounds__(kThreads) void ef_qdq_kernel(
     const void* x, float* __restrict__ res, void* y, int64_t n_oct,
     const float* __restrict__ st_ptr, uint64_t seed, uint64_t step, uint32_t* __restrict__ packed,
@@ -509,11 +513,11 @@ __global__ __launch_bounds__(kThreads) void ef_qdq_kernel(
   for (int k = 0; k < U; ++k) {
     const int64_t i = base + (int64_t)k * kThreads;
     const bool ok = i < n_oct;
-    if (ok) load8<BF16IN>(x, i, v[k]);
+    if (ok) load8<BF16IN, KEEP>(x, i, v[k]);
     else for (int j = 0; j < 8; ++j) v[k][j] = 0.0f;
     if constexpr (RES) {
       float rr[8];
-      if (ok) load8<false>(res, i, rr);
+      if (ok) load8<false, KEEP>(res, i, rr);
       else for (int j = 0; j < 8; ++j) rr[j] = 0.0f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) v[k][j] = v[k][j] + rr[j];
@@ -612,13 +616,13 @@ void launch_quantize_t(bool sr, const void* x, int64_t n_oct, const float* ts, u
                        packed, scales);
 }
 
-template <bool BF16IN, bool BF16OUT>
-void launch_ef_t(bool res, bool sr, bool codes, const void* x, float* r, void* y, int64_t n_oct,
+template <bool BF16IN, bool BF16OUT, bool KEEP>
+void launch_ef_k(bool res, bool sr, bool codes, const void* x, float* r, void* y, int64_t n_oct,
                  const float* ts, uint64_t seed, uint64_t step, uint32_t* packed, uint8_t* scales,
                  hipStream_t st) {
   const dim3 g((unsigned)blocks_for(n_oct, 1));
 #define FP4MI_EF(RES, SR, CODES)                                                                 \
-  hipLaunchKernelGGL((ef_qdq_kernel<BF16IN, BF16OUT, RES, SR, CODES>), g, dim3(kThreads),      \
+  hipLaunchKernelGGL((ef_qdq_kernel<BF16IN, BF16OUT, RES, SR, CODES, KEEP>), g, dim3(kThreads), \
                      0, st, x, r, y, n_oct, ts, seed, step, packed, scales)
   if (res) {
     if (sr) { if (codes) FP4MI_EF(true, true, true); else FP4MI_EF(true, true, false); }
@@ -628,6 +632,14 @@ void launch_ef_t(bool res, bool sr, bool codes, const void* x, float* r, void* y
     else    { if (codes) FP4MI_EF(false, false, true); else FP4MI_EF(false, false, false); }
   }
 #undef FP4MI_EF
+}
+
+template <bool BF16IN, bool BF16OUT>
+void launch_ef_t(bool res, bool sr, bool codes, bool given, const void* x, float* r, void* y,
+                 int64_t n_oct, const float* ts, uint64_t seed, uint64_t step, uint32_t* packed,
+                 uint8_t* scales, hipStream_t st) {
+  if (given) launch_ef_k<BF16IN, BF16OUT, true>(res, sr, codes, x, r, y, n_oct, ts, seed, step, packed, scales, st);
+  else launch_ef_k<BF16IN, BF16OUT, false>(res, sr, codes, x, r, y, n_oct, ts, seed, step, packed, scales, st);
 }
 
 // Exact grids must fit the x dimension of a launch.
@@ -764,12 +776,13 @@ extern "C" int fp4_errfeedback_qdq(const void* x, int dtype, int64_t rows, int64
   }
   uint32_t* pk = reinterpret_cast<uint32_t*>(packed);
   const bool res = residual != nullptr;
+  const bool given = tscale_mode == FP4_TSCALE_GIVEN;
   if (bf16) {
-    if (obf16) launch_ef_t<true, true>(res, sr, codes, x, residual, y, n_oct, tensor_scale, seed, step, pk, scales, st);
-    else       launch_ef_t<true, false>(res, sr, codes, x, residual, y, n_oct, tensor_scale, seed, step, pk, scales, st);
+    if (obf16) launch_ef_t<true, true>(res, sr, codes, given, x, residual, y, n_oct, tensor_scale, seed, step, pk, scales, st);
+    else       launch_ef_t<true, false>(res, sr, codes, given, x, residual, y, n_oct, tensor_scale, seed, step, pk, scales, st);
   } else {
-    if (obf16) launch_ef_t<false, true>(res, sr, codes, x, residual, y, n_oct, tensor_scale, seed, step, pk, scales, st);
-    else       launch_ef_t<false, false>(res, sr, codes, x, residual, y, n_oct, tensor_scale, seed, step, pk, scales, st);
+    if (obf16) launch_ef_t<false, true>(res, sr, codes, given, x, residual, y, n_oct, tensor_scale, seed, step, pk, scales, st);
+    else       launch_ef_t<false, false>(res, sr, codes, given, x, residual, y, n_oct, tensor_scale, seed, step, pk, scales, st);
   }
   return launch_status();
 }
