@@ -318,6 +318,22 @@ def breakdown(args, torch, fp4, np, synth, deferred):
         oracle=o_sr)
     del xs, ps, ss, ys
 
+    # MXFP4 with fp32 activations: quantize from fp32, dequantize to fp32 (4096 x 7168, 4 sets)
+    R, C = 4096, 7168
+    n = R * C
+    xs = [torch.randn((R, C), generator=g, device="cuda") * 0.5 for _ in range(4)]
+    ps = [torch.empty((R, C // 2), dtype=torch.uint8, device="cuda") for _ in range(4)]
+    ss = [torch.empty((R, C // 32), dtype=torch.uint8, device="cuda") for _ in range(4)]
+    ys = [torch.empty((R, C), dtype=torch.float32, device="cuda") for _ in range(4)]
+    nb = 4 * n + n // 2 + n // 32
+    add("mxfp4_quantize(rtn) f32 in", "4096x7168 fp32", nb,
+        timed(lambda k: fp4.fp4_quantize(xs[k % 4], "mxfp4", "rtn", packed=ps[k % 4], scales=ss[k % 4]),
+              iters))
+    add("mxfp4_dequantize f32 out", "4096x7168 fp32", nb,
+        timed(lambda k: fp4.fp4_dequantize(ps[k % 4], ss[k % 4], R, C, "mxfp4", None, torch.float32,
+                                           ys[k % 4]), iters))
+    del xs, ps, ss, ys
+
     # C3: FP4Quant codec on the 8192 x 4096 TP tensor, G = 64 and 256
     tb = synth.tp_tensor()
     R, C = tb.shape

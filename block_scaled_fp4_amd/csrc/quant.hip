@@ -235,8 +235,10 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
       ra[k] = ok ? ld_u32x4(static_cast<const uint8_t*>(x) + i * 16) : u32x4{0u, 0u, 0u, 0u};
     } else {
       const uint8_t* p = static_cast<const uint8_t*>(x) + i * 32;
-      ra[k] = ok ? ld_u32x4(p) : u32x4{0u, 0u, 0u, 0u};
-      rb[k] = ok ? ld_u32x4(p + 16) : u32x4{0u, 0u, 0u, 0u};
+      // MXFP4 reads the two halves of an fp32 octet with plain loads (the
+      // line stays in L2 between the two instructions)
+      ra[k] = ok ? (MX ? ld_u32x4_keep(p) : ld_u32x4(p)) : u32x4{0u, 0u, 0u, 0u};
+      rb[k] = ok ? (MX ? ld_u32x4_keep(p + 16) : ld_u32x4(p + 16)) : u32x4{0u, 0u, 0u, 0u};
     }
   }
 #pragma unroll
@@ -345,7 +347,7 @@ __device__ __forceinline__ void mx_dequant_octet_hw(uint32_t w, uint32_t b, void
   } else {
     float v[8];
     e2m1x8_to_f32(w, scale, v);
-    store8<false>(y, i, v);
+    store8<false, true>(y, i, v);
   }
 }
 
@@ -387,7 +389,7 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(
 #pragma unroll
       for (int j = 0; j < 8; ++j) v[j] = v[j] * sdec;
     }
-    store8<BF16OUT>(y, i, v);
+    store8<BF16OUT, true>(y, i, v);
   }
 }
 
