@@ -652,7 +652,7 @@ def summarize_pmc(dirs, out, command):
     alg = 2 * n + n // 2 + n // 32
     # template arguments: <bf16 input, MX, SR, ...> and <bf16 output, MX, ...>
     q = next(k for k in fetch if k.startswith("quantize_kernel<true, true, false"))
-    d = next(k for k in fetch if k.startswith("dequantize_kernel<true, true"))
+    d = next(k for k in fetch if k.startswith("dequantize_kernel<true, "))
     lines = ["# rocprofv3 PMC summary: HBM traffic of the MXFP4 headline kernels (4096x7168 bf16)",
              f"# command: {command}",
              f"# copy calibration: FETCH_SIZE reads {f_copy:.0f} B for a {copy_bytes} B copy (x{kf:.4f}); "

@@ -73,9 +73,7 @@ __device__ __forceinline__ void load8(const void* base, int64_t i, float (&v)[8]
 }
 
 // Store 8 consecutive fp32 values as f32 or bf16 (RNE).
-// KEEP: the two 16-byte halves of an fp32 octet are written with plain
-// stores, so that the line a wave writes in two instructions can meet in L2.
-template <bool BF16, bool KEEP = false>
+template <bool BF16>
 __device__ __forceinline__ void store8(void* base, int64_t i, const float (&v)[8]) {
   if constexpr (BF16) {
     u32x4 w;
@@ -89,13 +87,8 @@ __device__ __forceinline__ void store8(void* base, int64_t i, const float (&v)[8
     a.z = __float_as_uint(v[2]); a.w = __float_as_uint(v[3]);
     b.x = __float_as_uint(v[4]); b.y = __float_as_uint(v[5]);
     b.z = __float_as_uint(v[6]); b.w = __float_as_uint(v[7]);
-    if constexpr (KEEP) {
-      *reinterpret_cast<u32x4*>(p) = a;
-      *reinterpret_cast<u32x4*>(p + 16) = b;
-    } else {
-      st_u32x4(p, a);
-      st_u32x4(p + 16, b);
-    }
+    st_u32x4(p, a);
+    st_u32x4(p + 16, b);
   }
 }
 

@@ -333,25 +333,20 @@ __global__ __launch_bounds__(kThreads) void nv_rtn_quantize_kernel(
 }
 
 // ----------------------------------------------------------- dequantize
-template <bool BF16OUT>
+// bf16 output of an MXFP4 octet with a normal scale byte (1 <= b <= 254).
 __device__ __forceinline__ void mx_dequant_octet_hw(uint32_t w, uint32_t b, void* y, int64_t i) {
-  // scale 2^(b-127) is a normal float whose exponent field is b (1 <= b <= 254)
+  // scale 2^(b-127) is a normal float whose exponent field is b
   const float scale = __uint_as_float(b << 23);
-  if constexpr (BF16OUT) {
-    u32x4 o;
-    o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
-    o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
-    o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
-    o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
-    st_u32x4(static_cast<uint8_t*>(y) + i * 16, o);
-  } else {
-    float v[8];
-    e2m1x8_to_f32(w, scale, v);
-    store8<false, true>(y, i, v);
-  }
+  u32x4 o;
+  o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+  o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+  o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+  o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+  st_u32x4(static_cast<uint8_t*>(y) + i * 16, o);
 }
 
-template <bool BF16OUT, bool MX, int U = 1>
+// bf16 output (fp32 output: dequantize_f32_kernel).
+template <bool MX, int U = 1>
 __global__ __launch_bounds__(kThreads) void dequantize_kernel(
     const uint32_t* __restrict__ packed, const uint8_t* __restrict__ scales,
     const float* __restrict__ st_ptr, int64_t n_oct, void* __restrict__ y) {
@@ -374,7 +369,7 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(
     float v[8];
     if constexpr (MX) {
       if (b[k] - 1u < 254u) {
-        mx_dequant_octet_hw<BF16OUT>(w[k], b[k], y, i);
+        mx_dequant_octet_hw(w[k], b[k], y, i);
         continue;
       }
       // UE8M0 0 (2^-127) and 0xFF (NaN) in software
@@ -389,7 +384,55 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(
 #pragma unroll
       for (int j = 0; j < 8; ++j) v[j] = v[j] * sdec;
     }
-    store8<BF16OUT, true>(y, i, v);
+    store8<true>(y, i, v);
+  }
+}
+
+// fp32 output: thread t of workgroup b handles quads q = b 256 U + t + 256 k
+// (k < U) of four elements: their two code bytes at 2 q and 16 output bytes
+// at 16 q, so every store instruction of a wave writes 1 KiB contiguously
+// (an octet per lane writes 32 bytes in two instructions, each half-filling
+// its lines).  The values are those of dequantize_kernel: the same scaled
+// converter, and UE8M0 bytes 0 and 0xFF in software.
+template <bool MX, int U = 2>
+__global__ __launch_bounds__(kThreads) void dequantize_f32_kernel(
+    const uint16_t* __restrict__ packed, const uint8_t* __restrict__ scales,
+    const float* __restrict__ st_ptr, int64_t n_quad, float* __restrict__ y) {
+  const float st = MX ? 1.0f : *st_ptr;
+  const int64_t base = (int64_t)blockIdx.x * (kThreads * U) + threadIdx.x;
+  uint32_t w[U], b[U];
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+    const int64_t q = base + (int64_t)k * kThreads;
+    const bool ok = q < n_quad;
+    w[k] = ok ? (uint32_t)packed[q] : 0u;
+    b[k] = ok ? scales[q >> (MX ? 3 : 2)] : 0u;
+  }
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+    const int64_t q = base + (int64_t)k * kThreads;
+    if (q >= n_quad) continue;
+    float v[4];
+    if (!MX || b[k] - 1u < 254u) {
+      // MXFP4: 2^(b-127) is the normal float with exponent field b
+      const float scale = MX ? __uint_as_float(b[k] << 23) : 1.0f;
+      const f32x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[k], scale, 0);
+      const f32x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[k], scale, 1);
+      v[0] = lo.x; v[1] = lo.y; v[2] = hi.x; v[3] = hi.y;
+      if constexpr (!MX) {
+        const float sdec = e4m3_value_signed(b[k]) * st;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = v[j] * sdec;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float e = e2m1_value((w[k] >> (4 * j)) & 15u);
+        v[j] = (b[k] == 255u) ? __builtin_nanf("") : __builtin_amdgcn_ldexpf(e, -127);
+      }
+    }
+    st_u32x4(y + 4 * q, u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                              __float_as_uint(v[3])});
   }
 }
 
@@ -723,11 +766,15 @@ extern "C" int fp4_dequantize(const uint8_t* packed, const uint8_t* scales,
   const dim3 g((unsigned)blocks_for(n_oct, U));
   const uint32_t* pk = reinterpret_cast<const uint32_t*>(packed);
   if (out_dtype == FP4_DTYPE_BF16) {
-    if (mx) hipLaunchKernelGGL((dequantize_kernel<true, true, U>), dim3(g), dim3(kThreads), 0, st, pk, scales, tensor_scale, n_oct, y);
-    else    hipLaunchKernelGGL((dequantize_kernel<true, false, U>), dim3(g), dim3(kThreads), 0, st, pk, scales, tensor_scale, n_oct, y);
+    if (mx) hipLaunchKernelGGL((dequantize_kernel<true, U>), dim3(g), dim3(kThreads), 0, st, pk, scales, tensor_scale, n_oct, y);
+    else    hipLaunchKernelGGL((dequantize_kernel<false, U>), dim3(g), dim3(kThreads), 0, st, pk, scales, tensor_scale, n_oct, y);
   } else {
-    if (mx) hipLaunchKernelGGL((dequantize_kernel<false, true, U>), dim3(g), dim3(kThreads), 0, st, pk, scales, tensor_scale, n_oct, y);
-    else    hipLaunchKernelGGL((dequantize_kernel<false, false, U>), dim3(g), dim3(kThreads), 0, st, pk, scales, tensor_scale, n_oct, y);
+    const int64_t n_quad = 2 * n_oct;
+    const dim3 g4((unsigned)blocks_for(n_quad, U));
+    const uint16_t* p16 = reinterpret_cast<const uint16_t*>(packed);
+    float* yf = static_cast<float*>(y);
+    if (mx) hipLaunchKernelGGL((dequantize_f32_kernel<true, U>), g4, dim3(kThreads), 0, st, p16, scales, tensor_scale, n_quad, yf);
+    else    hipLaunchKernelGGL((dequantize_f32_kernel<false, U>), g4, dim3(kThreads), 0, st, p16, scales, tensor_scale, n_quad, yf);
   }
   return launch_status();
 }
