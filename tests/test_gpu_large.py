@@ -52,6 +52,13 @@ def test_mxfp4_roundtrip_past_2_32_elements():
     np.testing.assert_array_equal(host(s[torch.tensor(ids, device="cuda")]), rs)
     np.testing.assert_array_equal(host_bf16(y[torch.tensor(ids, device="cuda")]),
                                   mxfp4.dequantize(rp, rs, "bf16"))
+    # the fp32 receiver too (16 GiB of output, quads past index 2^31)
+    del y, x
+    _need_memory(R * C * 4)
+    yf = m.fp4_dequantize(p, s, R, C, "mxfp4", None, torch.float32)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(yf[torch.tensor(ids, device="cuda")]).view(np.uint32),
+                                  np.asarray(mxfp4.dequantize(rp, rs, "f32"), np.float32).view(np.uint32))
 
 
 def test_nvfp4_sr_counters_past_2_34_elements():
