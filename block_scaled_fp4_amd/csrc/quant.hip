@@ -278,6 +278,62 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
   }
 }
 
+// ------------------------------------------------ MXFP4 from fp32
+// Thread t of workgroup b handles quads q = b 256 U + t + 256 k (k < U) of
+// four elements: 16 input bytes at 16 q (one contiguous 1 KiB per load
+// instruction of a wave), two code bytes at 2 q.  A 32-element block is 8
+// consecutive lanes; its absmax takes three exchanges.  Codes as in
+// quantize_kernel: q = x * 2^(127 - b) exactly, then the scaled converter
+// (RTN) or e2m1_sr_mag with the draws of elements 4 q .. 4 q + 3, which are
+// the four words of Philox counter q.
+template <bool SR, bool WIDE, int U = 2>
+__global__ __launch_bounds__(kThreads) void mx_quantize_f32_kernel(
+    const float* __restrict__ x, int64_t n_quad, uint64_t seed, uint64_t step,
+    uint16_t* __restrict__ packed, uint8_t* __restrict__ scales) {
+  const int64_t base = (int64_t)blockIdx.x * (kThreads * U) + threadIdx.x;
+  u32x4 a[U];
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+    const int64_t q = base + (int64_t)k * kThreads;
+    a[k] = q < n_quad ? ld_u32x4(x + 4 * q) : u32x4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+    const int64_t q = base + (int64_t)k * kThreads;
+    const float v[4] = {__uint_as_float(a[k].x), __uint_as_float(a[k].y), __uint_as_float(a[k].z),
+                        __uint_as_float(a[k].w)};
+    float am = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+    am = fmaxf(am, lane_xor1(am));                  // every lane takes part in the exchanges
+    am = fmaxf(am, lane_xor2(am));
+    am = fmaxf(am, __shfl_xor(am, 4));
+    const uint32_t scode = mx_scale_byte(am);
+    const int shift = 127 - (int)scode;
+    uint32_t code;
+    if constexpr (SR) {
+      uint32_t c0 = (uint32_t)q, c1 = WIDE ? (uint32_t)((uint64_t)q >> 32) : 0u;
+      uint32_t c2 = (uint32_t)step, c3 = (uint32_t)(step >> 32);
+      philox4x32_10(c0, c1, c2, c3, (uint32_t)seed, (uint32_t)(seed >> 32));
+      const uint32_t u[4] = {c0 >> 8, c1 >> 8, c2 >> 8, c3 >> 8};
+      code = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float qv = __builtin_amdgcn_ldexpf(v[j], shift);
+        // an exactly positive scaled value that underflowed still rounds up when u = 0
+        const bool extra = (qv == 0.0f) && (v[j] != 0.0f) && (u[j] == 0u);
+        code |= (e2m1_sr_mag(fabsf(qv), u[j], extra) | sign_nibble(v[j])) << (4 * j);
+      }
+    } else {
+      const float q0 = __builtin_amdgcn_ldexpf(v[0], shift), q1 = __builtin_amdgcn_ldexpf(v[1], shift);
+      const float q2 = __builtin_amdgcn_ldexpf(v[2], shift), q3 = __builtin_amdgcn_ldexpf(v[3], shift);
+      code = cvt_fp4x2_f32<1>(cvt_fp4x2_f32<0>(0u, q0, q1, 1.0f), q2, q3, 1.0f);
+    }
+    if (q < n_quad) {
+      packed[q] = (uint16_t)code;
+      if ((q & 7) == 0) scales[q >> 3] = (uint8_t)scode;
+    }
+  }
+}
+
 // ------------------------------------------------ NVFP4 RTN quantize
 // Scale and codes from the division-free quotients, which are exact
 // wherever S_t lies in [2^-100, 2^100] and the block's raw scale quotient is
@@ -645,6 +701,17 @@ int launch_tensor_scale(const void* x, bool bf16, const float* res, int64_t n_oc
 template <bool BF16, bool MX>
 void launch_quantize_t(bool sr, const void* x, int64_t n_oct, const float* ts, uint64_t seed,
                        uint64_t step, uint32_t* packed, uint8_t* scales, hipStream_t st) {
+  if constexpr (MX && !BF16) {
+    // fp32 input: one lane per four elements
+    const int64_t n_quad = 2 * n_oct;
+    const dim3 g4((unsigned)blocks_for(n_quad, 2));
+    const float* xf = static_cast<const float*>(x);
+    uint16_t* p16 = reinterpret_cast<uint16_t*>(packed);
+    if (!sr) hipLaunchKernelGGL((mx_quantize_f32_kernel<false, false>), g4, dim3(kThreads), 0, st, xf, n_quad, seed, step, p16, scales);
+    else if (n_quad <= (int64_t(1) << 32)) hipLaunchKernelGGL((mx_quantize_f32_kernel<true, false>), g4, dim3(kThreads), 0, st, xf, n_quad, seed, step, p16, scales);
+    else hipLaunchKernelGGL((mx_quantize_f32_kernel<true, true>), g4, dim3(kThreads), 0, st, xf, n_quad, seed, step, p16, scales);
+    return;
+  }
   const dim3 g((unsigned)blocks_for(n_oct, kOctets<BF16>));
   // SR counters 2 i + 1 below 2^32: their second word is 0 throughout
   if (sr && 2 * n_oct <= (int64_t(1) << 32))

@@ -193,3 +193,25 @@ def test_fp4quant_sr_counters_past_2_34_elements():
     ids = [0, R // 3, R - 65, R - 64, R - 1]            # the last 64 rows lie past 2^34
     t = torch.tensor(ids, device="cuda")
     check_encode_sr(host(p[t]), host(s1[t]), host(s2[t]), _rows(x, ids), G, seed, step, row_ids=ids)
+
+
+def test_mxfp4_sr_from_fp32_past_2_34_elements():
+    """MXFP4 stochastic rounding from fp32 over 2^34 + 2^21 elements (64 GiB):
+    the four-element lanes of the last rows draw from Philox counters with a
+    non-zero high word.  Sampled rows, including the last, bit-exact."""
+    m = need_gpu()
+    R, C = (1 << 19) + 64, 1 << 15
+    _need_memory(R * C * (4 + 0.5 + 1 / 32))
+    x = torch.empty((R, C), dtype=torch.float32, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(16)
+    x.normal_(0.0, 2.0, generator=g)
+    seed, step = 0x0FEDCBA987654321, (1 << 35) + 9
+    p, s, _ = m.fp4_quantize(x, "mxfp4", "sr", seed=seed, step=step)
+    torch.cuda.synchronize()
+    ids = [0, R // 3, R - 65, R - 64, R - 1]            # the last 64 rows lie past 2^34
+    t = torch.tensor(ids, device="cuda")
+    xs = host(x[t])
+    rp, rs = mxfp4.quantize_packed(xs, "sr", seed=seed, step=step, row_ids=ids)
+    np.testing.assert_array_equal(host(s[t]), rs)
+    np.testing.assert_array_equal(host(p[t]), rp)
