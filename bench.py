@@ -329,10 +329,15 @@ def breakdown(args, torch, fp4, np, synth, deferred):
     add("mxfp4_quantize(rtn) f32 in", "4096x7168 fp32", nb,
         timed(lambda k: fp4.fp4_quantize(xs[k % 4], "mxfp4", "rtn", packed=ps[k % 4], scales=ss[k % 4]),
               iters))
+    ts32 = torch.tensor([np.float32(1.0 / 2688)], dtype=torch.float32, device="cuda")
+    ss16 = [torch.empty((R, C // 16), dtype=torch.uint8, device="cuda") for _ in range(4)]
+    add("nvfp4_quantize(rtn,given) f32 in", "4096x7168 fp32", 4 * n + n // 2 + n // 16,
+        timed(lambda k: fp4.fp4_quantize(xs[k % 4], "nvfp4", "rtn", tscale="given", tensor_scale=ts32,
+                                         packed=ps[k % 4], scales=ss16[k % 4]), iters))
     add("mxfp4_dequantize f32 out", "4096x7168 fp32", nb,
         timed(lambda k: fp4.fp4_dequantize(ps[k % 4], ss[k % 4], R, C, "mxfp4", None, torch.float32,
                                            ys[k % 4]), iters))
-    del xs, ps, ss, ys
+    del xs, ps, ss, ys, ss16
 
     # C3: FP4Quant codec on the 8192 x 4096 TP tensor, G = 64 and 256
     tb = synth.tp_tensor()

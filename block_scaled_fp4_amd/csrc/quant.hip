@@ -388,6 +388,59 @@ __global__ __launch_bounds__(kThreads) void nv_rtn_quantize_kernel(
   }
 }
 
+// ------------------------------------------------ NVFP4 RTN from fp32
+// Four elements per lane as in mx_quantize_f32_kernel (a 16-element block is
+// 4 lanes: two DPP exchanges for its absmax); scale and codes as in
+// nv_rtn_quantize_kernel, with the IEEE fallback behind the same wave-uniform
+// branch.
+template <int U = 2>
+__global__ __launch_bounds__(kThreads) void nv_rtn_quantize_f32_kernel(
+    const float* __restrict__ x, int64_t n_quad, const float* __restrict__ st_ptr,
+    uint16_t* __restrict__ packed, uint8_t* __restrict__ scales) {
+  const float st = *st_ptr;
+  const bool newton = nv_newton_range(st);
+  const float rst = newton ? 1.0f / st : 0.0f;
+  const int64_t base = (int64_t)blockIdx.x * (kThreads * U) + threadIdx.x;
+  u32x4 a[U];
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+    const int64_t q = base + (int64_t)k * kThreads;
+    a[k] = q < n_quad ? ld_u32x4(x + 4 * q) : u32x4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+    const int64_t q = base + (int64_t)k * kThreads;
+    const float v[4] = {__uint_as_float(a[k].x), __uint_as_float(a[k].y), __uint_as_float(a[k].z),
+                        __uint_as_float(a[k].w)};
+    // block absmax: a non-negative float orders like its bit pattern
+    uint32_t amb = __float_as_uint(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+    amb = max(amb, (uint32_t)lane_xor1_i((int)amb));
+    amb = max(amb, (uint32_t)lane_xor2_i((int)amb));
+    const float am = __uint_as_float(amb);
+    bool ok;
+    NvScale s = nv_block_scale_newton(am, st, rst, &ok);
+    ok = ok && newton;
+    const float y = (s.sdec == 0.0f) ? 0.0f : recip_rn(s.sdec);
+    uint32_t code = cvt_fp4x2_f32<1>(cvt_fp4x2_f32<0>(0u, div_rn(v[0], s.sdec, y), div_rn(v[1], s.sdec, y), 1.0f),
+                                     div_rn(v[2], s.sdec, y), div_rn(v[3], s.sdec, y), 1.0f);
+    if (__ballot(!ok)) {                            // wave-uniform; extreme inputs only
+      if (!ok) {
+        s = nv_block_scale_exact(am, st);
+        code = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float qv = (s.sdec == 0.0f) ? __builtin_copysignf(0.0f, v[j]) : v[j] / s.sdec;  // IEEE division
+          code |= (e2m1_rtn_mag(fabsf(qv)) | sign_nibble(v[j])) << (4 * j);
+        }
+      }
+    }
+    if (q < n_quad) {
+      packed[q] = (uint16_t)code;
+      if ((q & 3) == 0) scales[q >> 2] = (uint8_t)s.code;
+    }
+  }
+}
+
 // ----------------------------------------------------------- dequantize
 // bf16 output of an MXFP4 octet with a normal scale byte (1 <= b <= 254).
 __device__ __forceinline__ void mx_dequant_octet_hw(uint32_t w, uint32_t b, void* y, int64_t i) {
@@ -723,6 +776,10 @@ void launch_quantize_t(bool sr, const void* x, int64_t n_oct, const float* ts, u
   else if (MX)
     hipLaunchKernelGGL((quantize_kernel<BF16, true, false>), g, dim3(kThreads), 0, st, x,
                        n_oct, ts, seed, step, packed, scales);
+  else if constexpr (!BF16)
+    hipLaunchKernelGGL((nv_rtn_quantize_f32_kernel<2>), dim3((unsigned)blocks_for(2 * n_oct, 2)),
+                       dim3(kThreads), 0, st, static_cast<const float*>(x), 2 * n_oct, ts,
+                       reinterpret_cast<uint16_t*>(packed), scales);
   else
     hipLaunchKernelGGL((nv_rtn_quantize_kernel<BF16>), g, dim3(kThreads), 0, st, x, n_oct, ts,
                        packed, scales);
