@@ -783,6 +783,7 @@ extern "C" int fp4quant_encode_ex(const void* x, int dtype, int64_t rows, int64_
       overlaps(s_rms, gb, s_abs, gb))
     return FP4_EOVERLAP;
   if (blocks_for(n / 8, 1) > 0x7FFFFFFF) return FP4_ESHAPE;
+  clear_stale_error();
   hipStream_t st = as_stream(stream);
   uint32_t* pk = reinterpret_cast<uint32_t*>(packed);
   const bool sr = rounding == FP4_ROUND_SR;
@@ -808,6 +809,7 @@ extern "C" int fp4quant_decode(const uint8_t* packed, const float* s_rms, const 
   if (overlaps(y, yb, packed, n / 2) || overlaps(y, yb, s_rms, gb) || overlaps(y, yb, s_abs, gb))
     return FP4_EOVERLAP;
   if (blocks_for(n / 8, 1) > 0x7FFFFFFF) return FP4_ESHAPE;
+  clear_stale_error();
   hipStream_t st = as_stream(stream);
   const uint32_t* pk = reinterpret_cast<const uint32_t*>(packed);
   if (out_dtype == FP4_DTYPE_BF16) launch_decode<true>(group, pk, s_rms, s_abs, n, y, st);

@@ -449,6 +449,7 @@ extern "C" int mxfp4_row_to_fp8_col(const uint8_t* packed, const uint8_t* scales
     if (overlaps(fp8_out, ob, ins[k], inn[k]) || overlaps(fp8_scales, scb, ins[k], inn[k]))
       return FP4_EOVERLAP;
   if (overlaps(fp8_out, ob, fp8_scales, scb)) return FP4_EOVERLAP;
+  clear_stale_error();
   return launch_fp8col_tiles(packed, scales_e8m0, token_offsets, num_experts, total_tokens,
                              hidden, fp8_out, fp8_scales, as_stream(stream));
 }
@@ -473,6 +474,7 @@ extern "C" int mxfp4_row_to_fp8_row(const uint8_t* packed, const uint8_t* scales
   const int64_t n_chunk = 2 * n_sub;
   const int64_t grid = (n_chunk + kThreads * kRowChunks - 1) / (kThreads * kRowChunks);
   if (grid > 0x7FFFFFFF) return FP4_ESHAPE;
+  clear_stale_error();
   hipLaunchKernelGGL(fp8row_kernel, dim3((unsigned)grid), dim3(kThreads), 0, as_stream(stream),
                      packed, reinterpret_cast<const uint32_t*>(scales_e8m0), n_chunk, fp8_out,
                      fp8_scales);

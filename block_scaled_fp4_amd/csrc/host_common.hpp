@@ -32,6 +32,13 @@ inline bool checked_count(int64_t rows, int64_t cols, int64_t* n) {
   return true;
 }
 
+// hipGetLastError() both reads and resets the calling thread's last error.
+// An entry point calls this once its arguments are valid and before its
+// first HIP call, so that launch_status() afterwards reports only errors
+// raised by that entry point's own launches, not one left by an earlier,
+// unrelated HIP call on the same thread.
+inline void clear_stale_error() { (void)hipGetLastError(); }
+
 inline int launch_status() {
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? FP4_OK : FP4_EHIP;

@@ -842,6 +842,7 @@ extern "C" int fp4_quantize(const void* x, int dtype, int64_t rows, int64_t cols
   if (!mx && (overlaps(tensor_scale, 4, x, xb) || overlaps(tensor_scale, 4, packed, pb) ||
               overlaps(tensor_scale, 4, scales, sb)))
     return FP4_EOVERLAP;
+  clear_stale_error();
   hipStream_t st = as_stream(stream);
   const bool bf16 = dtype == FP4_DTYPE_BF16, sr = rounding == FP4_ROUND_SR;
   const int64_t n_oct = n / 8;
@@ -882,6 +883,7 @@ extern "C" int fp4_dequantize(const uint8_t* packed, const uint8_t* scales,
   if (overlaps(y, yb, packed, n / 2) || overlaps(y, yb, scales, n / blk) ||
       (!mx && overlaps(y, yb, tensor_scale, 4)))
     return FP4_EOVERLAP;
+  clear_stale_error();
   hipStream_t st = as_stream(stream);
   const int64_t n_oct = n / 8;
   if (!grid_fits(n_oct)) return FP4_ESHAPE;
@@ -934,6 +936,7 @@ extern "C" int fp4_errfeedback_qdq(const void* x, int dtype, int64_t rows, int64
     for (int l = k + 1; l < 3; ++l)
       if (overlaps(outs[k], outn[k], outs[l], outn[l])) return FP4_EOVERLAP;
   }
+  clear_stale_error();
   hipStream_t st = as_stream(stream);
   const bool bf16 = dtype == FP4_DTYPE_BF16, obf16 = out_dtype == FP4_DTYPE_BF16;
   const bool sr = rounding == FP4_ROUND_SR, codes = packed != nullptr;

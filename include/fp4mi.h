@@ -136,8 +136,8 @@ int fp4quant_encode(const void* x, int dtype, int64_t rows, int64_t cols,
  *
  * FP4_ROUND_RTN is fp4quant_encode.  FP4_ROUND_SR is a variant the FP4Quant
  * article does not describe: "fp4-train"'s stochastic rounding (section "How
- * it works": between two grid points the upper one with probability equal
- * to the fractional distance) applied to z / s2, the draw of each
+ * it works": round up to the next grid point with probability
+ * (|q| - lo) / (hi - lo), otherwise down) applied to z / s2, the draw of each
  * transformed element keyed by (seed, step, its row-major index in the
  * tensor) with the same Philox4x32-10 stream layout as fp4_quantize.  Scales
  * are those of RTN.  Arguments as fp4quant_encode; rounding outside

@@ -20,7 +20,7 @@ a step open, the reading taken is stated in the docstring and marked
 "[reading]".  Pins against facts outside the oracle live in ``tests/``.
 
 Parity status: every function here is pinned by at least one test that does
-not re-type its own formula, except the nibble order inside a packed byte
-(``pack_codes``), which no page fixes; it is "parity unpinned" and is held
-only by the OCP/PyTorch ``float4_e2m1fn_x2`` convention plus round trips.
+not re-type its own formula.  The nibble order inside a packed byte
+(``pack_codes``), which no page fixes, is pinned to ROCm's host-side fp4x2
+storage conversion (hip/hip_fp4.h), an implementation outside this package.
 """

@@ -92,8 +92,9 @@ def e2m1_sr_margin(q, u):
 def e2m1_sr(q, u):
     """Stochastic rounding onto the E2M1 grid.
 
-    "fp4-train", "How it works": between two grid points the higher is chosen
-    with probability equal to the fractional distance.  [reading] Work on the
+    "fp4-train", "How it works": a value lying between two neighbouring grid
+    points rounds up with a probability proportional to how far it sits above
+    the lower point, which makes the rounding unbiased.  [reading] Work on the
     magnitude |q|: lo = largest grid value <= |q|, hi = the next one; the
     result is hi iff u < (|q| - lo) / (hi - lo), with u in [0, 1) supplied by
     the caller; |q| >= 6 gives 6.  The sign is copied from q.
@@ -119,9 +120,10 @@ def pack_codes(codes):
     """Two 4-bit codes per byte along the last axis.
 
     "fp4-train" ("How it works") and the FP4Quant article ("Making
-    compression cheap enough to help") store two codes per byte.  [reading,
-    parity unpinned by the pages] element 2j goes to the low nibble and
-    element 2j+1 to the high nibble of byte j."""
+    compression cheap enough to help") store two codes per byte.  [reading:
+    no page fixes the order] element 2j goes to the low nibble and element
+    2j+1 to the high nibble of byte j, the order of the fp4x2 storage type
+    of ROCm's hip_fp4.h (pinned against its host conversion in the tests)."""
     c = np.asarray(codes).astype(np.uint8)
     assert c.shape[-1] % 2 == 0
     return (c[..., 0::2] & 0xF) | ((c[..., 1::2] & 0xF) << 4)

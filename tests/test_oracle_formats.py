@@ -211,3 +211,42 @@ def test_e2m1_sr_margin_is_distance_to_first_decision_change():
 
     brute = np.minimum(first_change(1.0), first_change(-1.0))
     np.testing.assert_allclose(F.e2m1_sr_margin(q, u), brute, rtol=0, atol=1e-12)
+
+
+def _rocm_fp4x2(pairs):
+    """Bytes from ROCm's host-side fp4x2 packing of float pairs (first element
+    of the pair is the .x component)."""
+    import os
+    import shutil
+    import subprocess
+    import tempfile
+    hipcc = next((c for c in ("/opt/rocm/bin/hipcc", shutil.which("hipcc")) if c and os.path.exists(c)),
+                 None)
+    if hipcc is None or not os.path.exists("/opt/rocm/include/hip/hip_fp4.h"):
+        pytest.skip("hipcc or hip_fp4.h missing")
+    src = os.path.join(os.path.dirname(__file__), "hip_fp4x2_ref.cpp")
+    with tempfile.TemporaryDirectory() as d:
+        exe = os.path.join(d, "ref")
+        subprocess.run([hipcc, "-O1", "-std=c++17", src, "-o", exe], check=True, capture_output=True)
+        inp = "".join(f"{a!r} {b!r}\n" for a, b in pairs)
+        out = subprocess.run([exe], input=inp, capture_output=True, text=True, check=True).stdout
+    return np.array([int(t) for t in out.split()], dtype=np.uint8)
+
+
+def test_pack_order_matches_rocm_fp4x2_storage():
+    """The packed layout (two codes per byte, "fp4-train" "How it works";
+    the FP4Quant article's "Making compression cheap enough to help") against
+    an implementation outside the oracle: ROCm's fp4x2 storage type puts the
+    first element of a pair in the low nibble.  Every pair of grid values
+    (16 x 16 codes, so no rounding is involved) pins the nibble order and the
+    sign bit; random pairs inside [-6, 6] also pin e2m1_rtn away from ties."""
+    grid = F.e2m1_decode(np.arange(16))
+    a, b = np.meshgrid(np.arange(16), np.arange(16), indexing="ij")
+    pairs = [(float(grid[i]), float(grid[j])) for i, j in zip(a.ravel(), b.ravel())]
+    rng = np.random.default_rng(11)
+    r = rng.uniform(-6.0, 6.0, size=(4000, 2)).astype(np.float32)
+    pairs += [(float(x), float(y)) for x, y in r]
+    got = _rocm_fp4x2(pairs)
+    codes = np.stack([np.arange(16)[a.ravel()], np.arange(16)[b.ravel()]], axis=-1).astype(np.uint8)
+    np.testing.assert_array_equal(got[:256], F.pack_codes(codes).ravel())
+    np.testing.assert_array_equal(got[256:], F.pack_codes(F.e2m1_rtn(r)).ravel())
