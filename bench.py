@@ -50,54 +50,80 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+# What each breakdown row is judged against.
+BOUNDS = {
+    "hbm": "HBM peak (8 TB/s) on algorithmic bytes: every input read once, every output written once",
+    "hbm_two_pass": "HBM peak on the bytes of both passes: the tensor-scale (amax) pass reads the "
+                    "input once more before the encode pass",
+    "alu": "VALU issue rate (Philox4x32-10 draws or transform butterflies per element exceed the "
+           "HBM time); the HBM fraction is given for reference and the VALU counters are in profiles/",
+    "launch": "launch latency: the tensor is too small to reach streaming bandwidth",
+}
+
 # ------------------------------------------------------------------ timing
-def graph_time(torch, fn, reps, replays=5, check=None):
-    """Mean duration of one fn(k) call: `reps` calls (k = 0..reps-1) are
-    captured in one HIP graph and the graph is replayed `replays` times
-    between HIP events recorded on the launch stream.  Host launch overhead
-    is thus excluded, as it would be for a graph-captured caller.  Falls back
-    to eager launches (events around the loop) if capture is refused."""
-    for k in range(min(reps, 3)):
+def graph_time(torch, fn, calls, chunk, check=None):
+    """Mean duration of one fn(k) call over exactly `calls` calls
+    (k = 0 .. calls - 1).  The calls are captured in ceil(calls / chunk)
+    HIP graphs (call k in graph k // chunk, so buffer rotation by k carries
+    across graphs); each graph is replayed once untimed, `check` runs, and
+    then every graph is replayed once, in order, between two HIP events on
+    the launch stream.  Host launch overhead is thus excluded, as for a
+    graph-captured caller.  Falls back to eager launches (events around the
+    loop) if capture is refused."""
+    calls = max(1, calls)
+    chunk = max(1, min(chunk, calls))
+    for k in range(min(calls, 3)):
         fn(k)
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     try:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for k in range(reps):
-                fn(k)
-        g.replay()
+        graphs = []
+        for g0 in range(0, calls, chunk):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for k in range(g0, min(calls, g0 + chunk)):
+                    fn(k)
+            graphs.append(g)
+        for g in graphs:
+            g.replay()
         torch.cuda.synchronize()
         if check:
             check()
         a.record()
-        for _ in range(replays):
+        for g in graphs:
             g.replay()
         b.record()
         torch.cuda.synchronize()
-        return a.elapsed_time(b) / (reps * replays), "graph"
+        return a.elapsed_time(b) / calls, f"{len(graphs)} graphs"
     except Exception as e:                      # capture unsupported: time eagerly
         log(f"[bench] graph capture failed ({e}); timing eagerly")
         torch.cuda.synchronize()
         a.record()
-        for _ in range(replays):
-            for k in range(reps):
-                fn(k)
+        for k in range(calls):
+            fn(k)
         b.record()
         torch.cuda.synchronize()
-        return a.elapsed_time(b) / (reps * replays), "eager"
+        return a.elapsed_time(b) / calls, "eager"
 
 
 # --------------------------------------------------------------- headline
 def headline(args, torch, fp4, np, synth):
+    """Step k: quantize buffer set k (bf16 -> codes + UE8M0) and dequantize
+    set k + LAG (codes + UE8M0 -> bf16), over `nsets` rotating sets.  The
+    dequantize thus reads codes written LAG steps (> 2 steps' traffic, more
+    than the 256 MB Infinity Cache) earlier, not the ones just written, and
+    every input is read from HBM."""
     rows, cols = 4096, 7168
     n = rows * cols
     q_bytes = 2 * n + n // 2 + n // 32          # read bf16, write codes + UE8M0
     dq_bytes = n // 2 + n // 32 + 2 * n         # read codes + UE8M0, write bf16
+    dq_in = n // 2 + n // 32
     log(f"[bench] generating {rows}x{cols} moe_dispatch input")
     xb = synth.moe_dispatch(rows, cols, seed=2)
     x0 = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).cuda()
-    nsets = args.sets
+    # enough sets that the dequantize inputs alone rotate over >= 512 MB
+    nsets = max(args.sets, -(-(512 << 20) // dq_in))
+    lag = 3
     sets = []
     for _ in range(nsets):
         sets.append(dict(x=x0.clone(),
@@ -105,14 +131,15 @@ def headline(args, torch, fp4, np, synth):
                          s=torch.empty((rows, cols // 32), dtype=torch.uint8, device="cuda"),
                          y=torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda")))
     foot = nsets * (q_bytes + 2 * n)
-    log(f"[bench] {nsets} buffer sets, footprint {foot / 1e6:.0f} MB")
+    log(f"[bench] {nsets} buffer sets, footprint {foot / 1e6:.0f} MB; quantize inputs rotate over "
+        f"{nsets * 2 * n / 1e6:.0f} MB, dequantize inputs over {nsets * dq_in / 1e6:.0f} MB")
 
     def quant(k):
         S = sets[k % nsets]
         fp4.fp4_quantize(S["x"], "mxfp4", "rtn", packed=S["p"], scales=S["s"])
 
     def dequant(k):
-        S = sets[k % nsets]
+        S = sets[(k + lag) % nsets]
         fp4.fp4_dequantize(S["p"], S["s"], rows, cols, "mxfp4", y=S["y"])
 
     def step(k):
@@ -120,6 +147,8 @@ def headline(args, torch, fp4, np, synth):
         dequant(k)
 
     if args.profile_mode == "headline":
+        for k in range(nsets):
+            quant(k)
         for k in range(args.warmup + args.steps):
             step(k)
         torch.cuda.synchronize()
@@ -127,6 +156,8 @@ def headline(args, torch, fp4, np, synth):
         return None
 
     # eager reference outputs of every set, to check the graph replays against
+    for k in range(nsets):
+        quant(k)
     for k in range(nsets):
         step(k)
     torch.cuda.synchronize()
@@ -137,23 +168,26 @@ def headline(args, torch, fp4, np, synth):
             assert torch.equal(S["p"], p) and torch.equal(S["s"], s) and torch.equal(S["y"], y), \
                 "graph replay differs from the eager result"
 
-    reps = args.graph_steps
-    replays = max(1, args.steps // reps)
     for k in range(args.warmup):
         step(k)
     torch.cuda.synchronize()
-    ms_step, mode = graph_time(torch, step, reps, replays, check)
-    q_ms, _ = graph_time(torch, quant, reps, replays)
-    d_ms, _ = graph_time(torch, dequant, reps, replays)
+    # exactly --steps steps, in several graphs (at least four when steps allow)
+    chunk = max(1, min(args.graph_steps, args.steps // 4))
+    ms_step, mode = graph_time(torch, step, args.steps, chunk, check)
+    # per-kernel legs: every set at least twice
+    kcalls = max(args.steps, 2 * nsets)
+    q_ms, _ = graph_time(torch, quant, kcalls, args.graph_steps)
+    d_ms, _ = graph_time(torch, dequant, kcalls, args.graph_steps)
     check()
     # achievable-bandwidth reference: a plain device copy of the bf16 input
     # (read 2n + write 2n bytes) over the same rotating buffer sets
-    c_ms, _ = graph_time(torch, lambda k: sets[k % nsets]["y"].copy_(sets[k % nsets]["x"]), reps, replays)
-    steps = reps * replays
-    log(f"[bench] {mode}: step {ms_step * 1e3:.2f} us; quantize {q_ms * 1e3:.2f} us; "
-        f"dequantize {d_ms * 1e3:.2f} us ({steps} steps)")
+    c_ms, _ = graph_time(torch, lambda k: sets[k % nsets]["y"].copy_(sets[k % nsets]["x"]), kcalls,
+                         args.graph_steps)
+    log(f"[bench] {mode}: step {ms_step * 1e3:.2f} us ({args.steps} steps); quantize {q_ms * 1e3:.2f} us; "
+        f"dequantize {d_ms * 1e3:.2f} us ({kcalls} calls each)")
     return dict(rows=rows, cols=cols, n=n, q_bytes=q_bytes, dq_bytes=dq_bytes, ms_step=ms_step,
-                q_ms=q_ms, d_ms=d_ms, copy_GBps=4 * n / (c_ms * 1e-3) / 1e9, nsets=nsets, footprint=foot, xb=xb, steps=steps, mode=mode)
+                q_ms=q_ms, d_ms=d_ms, copy_GBps=4 * n / (c_ms * 1e-3) / 1e9, nsets=nsets, footprint=foot,
+                xb=xb, steps=args.steps, mode=mode, graph_chunk=chunk, kernel_calls=kcalls, lag=lag)
 
 
 def copy_probe(args, torch):
@@ -199,7 +233,7 @@ def breakdown(args, torch, fp4, np, synth, deferred):
         from oracle import nvfp4 as NV
 
     def timed(fn, reps):
-        return graph_time(torch, fn, reps, replays=3)[0]
+        return graph_time(torch, fn, 3 * reps, reps)[0]
 
     def leg(fn, nbytes, what, *fargs, prep=None, **fkw):
         """An oracle leg: fn(*fargs, **fkw) -- or fn(*prep()) when a prep
@@ -218,12 +252,20 @@ def breakdown(args, torch, fp4, np, synth, deferred):
     def nv_compute(x):
         return NV.quantize_packed(x, NV.tensor_scale(x))
 
-    def add(op, workload, nbytes, ms, note=None, oracle=None):
+    def add(op, workload, nbytes, ms, note=None, oracle=None, bound="hbm", extra_bytes=0):
         """oracle: (callable returning the algorithmic bytes of one call on a
-        host sample, description of the sample), timed single-threaded."""
+        host sample, description of the sample), timed single-threaded.
+        bound: what the row is judged against (BOUNDS); extra_bytes: bytes a
+        second pass moves beyond the algorithmic ones (the amax pass)."""
         gbs = nbytes / (ms * 1e-3) / 1e9
         e = dict(op=op, workload=workload, algorithmic_bytes=nbytes, us=round(ms * 1e3, 2),
-                 GBps=round(gbs, 1), frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4))
+                 GBps=round(gbs, 1), frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4),
+                 bound=bound, judged_against=BOUNDS[bound])
+        if extra_bytes:
+            two = (nbytes + extra_bytes) / (ms * 1e-3) / 1e9
+            e["two_pass_bytes"] = nbytes + extra_bytes
+            e["two_pass_GBps"] = round(two, 1)
+            e["frac_of_hbm_peak_two_pass"] = round(two / HBM_PEAK_GBS, 4)
         if note:
             e["note"] = note
         if with_oracle and oracle is not None:
@@ -274,9 +316,10 @@ def breakdown(args, torch, fp4, np, synth, deferred):
         o_dq = leg(NV.dequantize, nb, "the whole 256x2048 block", prep=prep_c1)
     add("nvfp4_quantize(rtn,compute)", "256x2048 bf16 weight block", nb,
         timed(lambda k: fp4.fp4_quantize(x, "nvfp4", "rtn", packed=p, scales=s, tensor_scale=ts), iters),
-        "3 launches: amax, reduction of the partial maxima, encode", oracle=o_q)
+        "3 launches: amax, reduction of the partial maxima, encode", oracle=o_q, bound="launch")
     add("nvfp4_dequantize", "256x2048 bf16 weight block", nb,
-        timed(lambda k: fp4.fp4_dequantize(p, s, R, C, "nvfp4", ts, y=y), iters), oracle=o_dq)
+        timed(lambda k: fp4.fp4_dequantize(p, s, R, C, "nvfp4", ts, y=y), iters), oracle=o_dq,
+        bound="launch")
 
     # C1 shape at 8192 x 8192: the NVFP4 bandwidth row (4 rotating sets, 690 MB,
     # so that the 256 MB Infinity Cache cannot serve one call's data to the next)
@@ -308,14 +351,15 @@ def breakdown(args, torch, fp4, np, synth, deferred):
     add("nvfp4_quantize(rtn,compute)", "8192x8192 bf16", nb,
         timed(lambda k: fp4.fp4_quantize(xs[k % NS], "nvfp4", "rtn", tensor_scale=ts,
                                          packed=ps[k % NS], scales=ss[k % NS]), iters),
-        "includes the amax pass (an extra read of x)", oracle=o_c)
+        "includes the amax pass (an extra read of x)", oracle=o_c, bound="hbm_two_pass",
+        extra_bytes=2 * n)
     add("nvfp4_dequantize", "8192x8192 bf16", nb,
         timed(lambda k: fp4.fp4_dequantize(ps[k % NS], ss[k % NS], R, C, "nvfp4", ts, y=ys[k % NS]), iters),
         oracle=o_d)
     add("nvfp4_quantize(sr,given)", "8192x8192 bf16", nb,
         timed(lambda k: fp4.fp4_quantize(xs[k % NS], "nvfp4", "sr", seed=1, step=k, tscale="given",
                                          tensor_scale=ts, packed=ps[k % NS], scales=ss[k % NS]), iters),
-        oracle=o_sr)
+        oracle=o_sr, bound="alu")
     del xs, ps, ss, ys
 
     # MXFP4 with fp32 activations: quantize from fp32, dequantize to fp32 (4096 x 7168, 4 sets)
@@ -360,7 +404,7 @@ def breakdown(args, torch, fp4, np, synth, deferred):
                        prep=lambda xq=xq, G=G: Q.encode(xq, G) + (G,))
         add(f"fp4quant_encode(G={G})", "8192x4096 bf16 TP tensor", nb,
             timed(lambda k: fp4.fp4quant_encode(xs[k % 4], G, pk[k % 4], s1[k % 4], s2[k % 4]), iters),
-            oracle=o_e)
+            oracle=o_e, bound="alu" if G >= 256 else "hbm")
         add(f"fp4quant_decode(G={G})", "8192x4096 bf16 TP tensor", nb,
             timed(lambda k: fp4.fp4quant_decode(pk[k % 4], s1[k % 4], s2[k % 4], R, C, G, y=ys[k % 4]),
                   iters), oracle=o_de)
@@ -371,7 +415,7 @@ def breakdown(args, torch, fp4, np, synth, deferred):
         add(f"fp4quant_encode_sr(G={G})", "8192x4096 bf16 TP tensor", nb,
             timed(lambda k: fp4.fp4quant_encode_ex(xs[k % 4], G, "sr", 5, k, pk[k % 4], s1[k % 4],
                                                    s2[k % 4]), iters),
-            "stochastic-rounding variant (Philox draws per element)", oracle=o_sr)
+            "stochastic-rounding variant (Philox draws per element)", oracle=o_sr, bound="alu")
     del xs, pk, s1, s2, ys, x
 
     # C4: SR + error feedback step on an 8192 x 8192 weight (x fp32, r fp32, W bf16)
@@ -393,7 +437,8 @@ def breakdown(args, torch, fp4, np, synth, deferred):
                    seed=4, step=1)
     add("errfeedback_qdq(sr,compute)", "8192x8192 fp32 x + fp32 r -> bf16 W", nb,
         timed(lambda k: fp4.fp4_errfeedback_qdq(xf, r, W, None, "sr", 4, k, "compute", ts), max(iters // 2, 5)),
-        "includes the amax pass over x + r (536,870,912 extra bytes read)", oracle=o_ec)
+        "includes the amax pass over x + r (536,870,912 extra bytes read)", oracle=o_ec,
+        bound="hbm_two_pass", extra_bytes=8 * n)
     add("errfeedback_qdq(sr,given)", "8192x8192 fp32 x + fp32 r -> bf16 W", nb,
         timed(lambda k: fp4.fp4_errfeedback_qdq(xf, r, W, None, "sr", 4, k, "given", ts), max(iters // 2, 5)),
         oracle=o_eg)
@@ -463,7 +508,7 @@ def size_sweep(args, torch, fp4, np):
 
         nb = 2 * n + n // 2 + n // 32
         for name, fn in (("quantize", quant), ("dequantize", dequant)):
-            ms, _ = graph_time(torch, fn, reps, replays=3)
+            ms, _ = graph_time(torch, fn, 3 * reps, reps)
             pts[name].append((rows, nb, ms * 1e3))
         log(f"[bench] sweep {rows:6d} x {cols}: {nsets:3d} sets; quantize {pts['quantize'][-1][2]:8.2f} us; "
             f"dequantize {pts['dequantize'][-1][2]:8.2f} us")
@@ -567,17 +612,42 @@ def cpu_baseline(xb, rows_chunk=512, min_seconds=10.0, max_seconds=30.0):
     one = nbytes / dt / 1e9
     one_sample = (f"{rows_done} rows ({rows_done / rows_total:.2f} passes over the "
                   f"{rows_total}x{xb.shape[1]} input, {rows_chunk}-row chunks), {dt:.1f} s")
-    procs = min(16, len(os.sched_getaffinity(0)))
+    affinity, model = host_cpus()
+    procs = min(CPU_SHARE, affinity)
+    host = {"affinity_cores": affinity, "cpu_model": model,
+            "cores_note": f"workers = min({CPU_SHARE}, affinity cores): a one-GPU job's share of "
+                          f"this host's CPUs is {CPU_SHARE}"}
     try:
         rate, passes, dtp = cpu_baseline_pool(xb, procs, min_seconds=min_seconds)
     except Exception as ex:                         # the pooled leg must not cost the GPU line
         log(f"[bench] pooled oracle failed ({ex}); reporting the single-core leg")
-        return {"value": round(one, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
-                "sample": f"quantize+dequantize of {one_sample}, single-threaded numpy"}
-    return {"value": round(rate, 6), "unit": "GB/s", "cores": procs, "kind": "oracle",
-            "sample": f"quantize+dequantize of the {rows_total}x{xb.shape[1]} input in 64-row chunks "
-                      f"over {procs} worker processes (one thread each), {passes} passes in {dtp:.1f} s",
-            "value_1core": round(one, 6), "sample_1core": one_sample}
+        return dict({"value": round(one, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                     "sample": f"quantize+dequantize of {one_sample}, single-threaded numpy"}, **host)
+    return dict({"value": round(rate, 6), "unit": "GB/s", "cores": procs, "kind": "oracle",
+                 "sample": f"quantize+dequantize of the {rows_total}x{xb.shape[1]} input in 64-row chunks "
+                           f"over {procs} worker processes (one thread each), {passes} passes in {dtp:.1f} s",
+                 "value_1core": round(one, 6), "sample_1core": one_sample}, **host)
+
+
+CPU_SHARE = 16
+
+
+def host_cpus():
+    """(CPUs this process may run on, CPU model name from /proc/cpuinfo)."""
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count() or 1
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return affinity, model
 
 
 # ------------------------------------------------------------ PMC summary
@@ -781,16 +851,19 @@ def main():
             "kernel": f"mxfp4 {dom} (4096x7168 bf16)", "algorithmic_bytes_per_launch": dom_bytes}
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
-        "steps": h["steps"], "warmup": args.warmup, "ms_per_step": round(h["ms_step"], 5),
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(h["ms_step"], 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "MXFP4 quantize+pack then dequantize of a 4096x7168 bf16 MoE dispatch "
                                "activation (Student-t(4)*0.5, 8 hot channels x30), RTN, UE8M0 scales",
                    "rows": h["rows"], "cols": h["cols"], "fmt": "mxfp4", "rounding": "rtn",
-                   "buffer_sets": h["nsets"], "footprint_bytes": h["footprint"]},
+                   "buffer_sets": h["nsets"], "footprint_bytes": h["footprint"],
+                   "dequantize_reads_set": f"k + {h['lag']} (codes written {h['lag']} steps earlier)"},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "kernels_us": {"quantize": round(h["q_ms"] * 1e3, 2), "dequantize": round(h["d_ms"] * 1e3, 2)},
-        "timing": f"HIP graph of {args.graph_steps} steps replayed, HIP events on the launch stream ({h['mode']})",
+        "timing": (f"exactly {args.steps} steps in {h['mode']} of up to {h['graph_chunk']} steps, each "
+                   f"replayed once between HIP events on the launch stream; per-kernel times over "
+                   f"{h['kernel_calls']} calls"),
         "roofline": roof,
         "copy_reference_GBps": round(h["copy_GBps"], 1),
     }

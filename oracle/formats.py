@@ -166,17 +166,15 @@ def e4m3_encode(x):
     if np.isnan(x).any():
         raise ValueError("NaN is outside the codec's contract")
     a = np.minimum(np.abs(x), E4M3_MAX)
-    flat = a.reshape(-1)
-    out = np.empty(flat.shape, dtype=np.uint8)
-    # chunk to bound memory of the distance matrix
-    for s in range(0, flat.size, 1 << 16):
-        blk = flat[s:s + (1 << 16)]
-        dist = np.abs(blk[:, None] - _E4M3_POS[None, :])
-        best = dist.min(axis=1, keepdims=True)
-        cand = dist == best
-        idx = np.arange(_E4M3_POS.size)
-        score = np.where(cand, np.where(idx % 2 == 0, 0, 1), 99)
-        out[s:s + blk.size] = np.argmin(score, axis=1)
+    # the representable magnitudes lo <= a < hi around a (lo = hi = 448 at the top)
+    k = np.searchsorted(_E4M3_POS, a, side="right")
+    lo = np.clip(k - 1, 0, _E4M3_POS.size - 1)
+    hi = np.clip(k, 0, _E4M3_POS.size - 1)
+    d_lo = a - _E4M3_POS[lo]
+    d_hi = _E4M3_POS[hi] - a
+    # the nearer one; on an exact tie the one with the even code
+    take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi != lo) & (hi % 2 == 0))
+    out = np.where(take_hi, hi, lo).astype(np.uint8)
     out = out.reshape(a.shape)
     return (out | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
 

@@ -78,34 +78,6 @@ def test_many_empty_experts_inside_one_tile():
     np.testing.assert_array_equal(s.view(np.uint32), rs.view(np.uint32))
 
 
-def test_full_size_zipf_shards_sampled_experts():
-    """65,536 tokens x 7168 in 256 Zipf(1.1) shards, random MXFP4 rows: the
-    whole conversion runs on the GPU; the oracle checks, per sampled expert,
-    every byte of two sampled FP8 block rows (256 channels) and the scales."""
-    m = need_gpu()
-    T, H, E = 65536, 7168, 256
-    counts, off = synth.expert_counts(T, E, seed=5)
-    packed, sb = synth.random_mxfp4(T, H, seed=5, scale_lo=110, scale_hi=140)
-    o, s = convert_gpu(m, packed, sb, off, H)
-    rng = np.random.default_rng(0)
-    experts = np.unique(np.concatenate([[0, 1, E - 1, E - 2], rng.choice(E, 6, replace=False)]))
-    HB = H // 128
-    for e in experts:
-        a, b = int(off[e]), int(off[e + 1])
-        n = b - a
-        if n == 0:
-            continue
-        blocks = np.unique([0, HB - 1, int(rng.integers(HB))])
-        for blk in blocks:
-            cols = slice(blk * 64, blk * 64 + 64)
-            scs = slice(blk * 4, blk * 4 + 4)
-            ro, rs = fp8col.convert(packed[a:b, cols], sb[a:b, scs], np.array([0, n], np.int64), 128)
-            got = o[H * a: H * b].reshape(H, n)[blk * 128: blk * 128 + 128]
-            np.testing.assert_array_equal(got.reshape(-1), ro)
-            gs = s[HB * a: HB * b].reshape(HB, n)[blk]
-            np.testing.assert_array_equal(gs.view(np.uint32), rs.view(np.uint32))
-
-
 @pytest.mark.parametrize("E", [2047, 2048, 2600])
 def test_expert_table_in_lds_and_in_global_memory(E):
     """Up to 2047 experts the expert lookups read a table in LDS, beyond that

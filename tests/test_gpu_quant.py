@@ -156,27 +156,6 @@ def test_nvfp4_bf16_input_exact_and_ambiguous_quotients():
         np.testing.assert_array_equal(p, rp)
 
 
-def test_nvfp4_rtn_8192x8192_compute_sampled_rows():
-    """The 8192 x 8192 NVFP4 RTN shape, computed S_t, in the launch the
-    bench times: S_t against the oracle's max over the whole tensor, then
-    every code and scale byte of 32 sampled rows, and their dequantized
-    values."""
-    m = need_gpu()
-    xb = synth.weight_block(8192, 8192, seed=11)
-    R, C = xb.shape
-    x_dev = dev_bf16(xb)
-    p, s, ts = run_quant(m, x_dev, "nvfp4")
-    st = nvfp4.tensor_scale(F.bf16_bits_to_f32(xb))
-    assert np.float32(ts) == st
-    rows = np.unique(np.concatenate([[0, R - 1], np.random.default_rng(11).choice(R, 30, replace=False)]))
-    x = F.bf16_bits_to_f32(xb[rows])
-    rp, rs = nvfp4.quantize_packed(x, st)
-    np.testing.assert_array_equal(s[rows], rs)
-    np.testing.assert_array_equal(p[rows], rp)
-    y = run_dequant(m, p, s, R, C, "nvfp4", ts)
-    np.testing.assert_array_equal(y[rows], nvfp4.dequantize(rp, rs, st, "bf16"))
-
-
 def test_nvfp4_exact_ties_with_computed_scale():
     """Elements that share the significand of the tensor's absmax A have
     x / s_dec = 2688 * 2^k / e4m3 in exact arithmetic, a rounding threshold
@@ -243,23 +222,6 @@ def test_nvfp4_dequantize_foreign_scale_bytes():
                 np.testing.assert_array_equal(y[~nan], ref[~nan])
             else:
                 assert_same_f32(y, ref)
-
-
-# ------------------------------------------------------------- MXFP4
-def test_mxfp4_moe_dispatch_full_size_sampled_rows():
-    """4096 x 7168 bf16 (Student-t, hot channels): every output byte of 48
-    sampled rows (first, last, random) vs the oracle; dequantize likewise."""
-    m = need_gpu()
-    xb = synth.moe_dispatch()
-    R, C = xb.shape
-    p, s, _ = run_quant(m, dev_bf16(xb), "mxfp4")
-    rows = np.unique(np.concatenate([[0, R - 1], np.random.default_rng(2).choice(R, 46, replace=False)]))
-    x = F.bf16_bits_to_f32(xb[rows])
-    rp, rs = mxfp4.quantize_packed(x)
-    np.testing.assert_array_equal(p[rows], rp)
-    np.testing.assert_array_equal(s[rows], rs)
-    y = run_dequant(m, p, s, R, C, "mxfp4")
-    np.testing.assert_array_equal(y[rows], mxfp4.dequantize(rp, rs, "bf16"))
 
 
 @pytest.mark.parametrize("rows,cols,dtype",
