@@ -9,7 +9,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fp4mi.h")
-LIB = os.path.join(ROOT, "block_scaled_fp4_amd", "libfp4mi.so")
+LIB = os.environ.get("FP4MI_SANITIZED_LIB") or os.path.join(ROOT, "block_scaled_fp4_amd", "libfp4mi.so")
 
 
 def declared_functions():
@@ -180,3 +180,114 @@ def test_product_code_never_reaches_the_oracle():
             elif f.endswith((".hip", ".hpp", ".h", ".cpp")):
                 src = open(path).read()
                 assert not re.search(r"^\s*#\s*include\s*[<\"][^>\"]*oracle", src, re.M), path
+
+
+# ------------------------------------------------ randomized invalid calls
+# Each case starts from a valid argument set (fake device addresses far
+# apart, so nothing overlaps) and breaks exactly one documented rule; the
+# call must return that rule's status without launching anything.  Run
+# under ASan/UBSan by test_abi_sanitized.py.
+GAP = 1 << 40
+
+
+def _quantize_case(rng, c):
+    fmt, dtype = int(rng.integers(2)), int(rng.integers(2))
+    blk = 32 if fmt else 16
+    a = dict(x=A, dtype=dtype, rows=int(rng.integers(1, 1 << 20)), cols=blk * int(rng.integers(1, 1 << 10)),
+             fmt=fmt, rnd=int(rng.integers(2)), tmode=int(rng.integers(2)), ts=A + 3 * GAP,
+             packed=A + GAP, scales=A + 2 * GAP)
+    muts = [("dtype", int(rng.choice([-1, 2, 3, 77])), "FP4_EDTYPE"),
+            ("fmt", int(rng.choice([-1, 2, 9])), "FP4_EINVAL"),
+            ("rnd", int(rng.choice([-1, 2, 5])), "FP4_EINVAL"),
+            ("rows", -int(rng.integers(1, 1 << 30)), "FP4_ESHAPE"),
+            ("cols", a["cols"] + int(rng.choice([1, 2, 8])) if fmt == 0 else a["cols"] + 16, "FP4_ESHAPE"),
+            ("rows", 1 << 40, "FP4_ESHAPE"),
+            ("x", None, "FP4_EINVAL"), ("packed", None, "FP4_EINVAL"), ("scales", None, "FP4_EINVAL"),
+            ("x", A + int(rng.choice([1, 2, 4, 8, 12])), "FP4_EALIGN"),
+            ("packed", A + GAP + int(rng.choice([1, 2, 3])), "FP4_EALIGN"),
+            ("packed", A + 16 * int(rng.integers(0, 4)), "FP4_EOVERLAP"),
+            ("scales", A + GAP + 4 * int(rng.integers(0, 8)), "FP4_EOVERLAP")]
+    if fmt == 0:
+        muts += [("tmode", int(rng.choice([-1, 2, 4])), "FP4_EINVAL"), ("ts", None, "FP4_EINVAL"),
+                 ("ts", A + 3 * GAP + 2, "FP4_EALIGN"), ("ts", A + 2 * GAP, "FP4_EOVERLAP")]
+    k, v, want = muts[int(rng.integers(len(muts)))]
+    a[k] = v
+    return lambda lib: _q(lib, **a), c[want], (k, v)
+
+
+def _encode_case(rng, c, ex):
+    G = int(1 << rng.integers(4, 11))
+    a = dict(x=A, dtype=int(rng.integers(2)), rows=int(rng.integers(1, 1 << 20)),
+             cols=G * int(rng.integers(1, 64)), G=G, rnd=int(rng.integers(2)), p=A + GAP, s1=A + 2 * GAP,
+             s2=A + 3 * GAP)
+    muts = [("dtype", 5, "FP4_EDTYPE"), ("G", int(rng.choice([0, 8, 48, 100, 2048, -64])), "FP4_EINVAL"),
+            ("rows", -3, "FP4_ESHAPE"), ("cols", a["cols"] + G // 2, "FP4_ESHAPE"),
+            ("x", None, "FP4_EINVAL"), ("s1", None, "FP4_EINVAL"), ("s2", None, "FP4_EINVAL"),
+            ("x", A + 4, "FP4_EALIGN"), ("s1", A + 2 * GAP + 1, "FP4_EALIGN"),
+            ("s1", A + 3 * GAP, "FP4_EOVERLAP"), ("p", A, "FP4_EOVERLAP")]
+    if ex:
+        muts.append(("rnd", int(rng.choice([-1, 2, 3])), "FP4_EINVAL"))
+    k, v, want = muts[int(rng.integers(len(muts)))]
+    a[k] = v
+
+    def call(lib):
+        if ex:
+            f = lib.fp4quant_encode_ex
+            f.argtypes = [P, I, I64, I64, I32, I, U64, U64, P, P, P, P]
+            return f(a["x"], a["dtype"], a["rows"], a["cols"], a["G"], a["rnd"], 1, 2, a["p"], a["s1"], a["s2"],
+                     None)
+        f = lib.fp4quant_encode
+        f.argtypes = [P, I, I64, I64, I32, P, P, P, P]
+        return f(a["x"], a["dtype"], a["rows"], a["cols"], a["G"], a["p"], a["s1"], a["s2"], None)
+    return call, c[want], (k, v)
+
+
+def _fp8_case(rng, c):
+    T, H, E = int(rng.integers(1, 1 << 20)), 128 * int(rng.integers(1, 64)), int(rng.integers(1, 1 << 12))
+    a = dict(p=A, s=A + GAP, off=A + 2 * GAP, E=E, T=T, H=H, o=A + 3 * GAP, sc=A + 4 * GAP)
+    muts = [("E", int(rng.choice([0, -1])), "FP4_EINVAL"), ("E", 1 << 26, "FP4_ESHAPE"),
+            ("T", -1, "FP4_ESHAPE"), ("T", 1 << 26, "FP4_ESHAPE"), ("H", H + 64, "FP4_ESHAPE"),
+            ("H", 0, "FP4_ESHAPE"), ("H", 1 << 21, "FP4_ESHAPE"), ("off", None, "FP4_EINVAL"),
+            ("p", None, "FP4_EINVAL"), ("sc", None, "FP4_EINVAL"), ("p", A + 8, "FP4_EALIGN"),
+            ("off", A + 2 * GAP + 4, "FP4_EALIGN"), ("o", A + 3 * GAP + 2, "FP4_EALIGN"),
+            ("o", A + GAP, "FP4_EOVERLAP"), ("sc", A + 3 * GAP + 128, "FP4_EOVERLAP")]
+    k, v, want = muts[int(rng.integers(len(muts)))]
+    a[k] = v
+
+    def call(lib):
+        f = lib.mxfp4_row_to_fp8_col
+        f.argtypes = [P, P, P, I32, I64, I64, P, P, P]
+        return f(a["p"], a["s"], a["off"], a["E"], a["T"], a["H"], a["o"], a["sc"], None)
+    return call, c[want], (k, v)
+
+
+def _ef_case(rng, c):
+    a = dict(x=A, dtype=int(rng.integers(2)), rows=int(rng.integers(1, 1 << 20)), cols=16 * int(rng.integers(1, 512)),
+             r=A + GAP, y=A + 2 * GAP, odt=int(rng.integers(2)), rnd=int(rng.integers(2)), tmode=int(rng.integers(2)),
+             ts=A + 3 * GAP, p=A + 4 * GAP, s=A + 5 * GAP)
+    muts = [("dtype", 3, "FP4_EDTYPE"), ("odt", -1, "FP4_EDTYPE"), ("rnd", 2, "FP4_EINVAL"),
+            ("tmode", 7, "FP4_EINVAL"), ("cols", a["cols"] + 8, "FP4_ESHAPE"), ("rows", -2, "FP4_ESHAPE"),
+            ("ts", None, "FP4_EINVAL"), ("y", None, "FP4_EINVAL"), ("s", None, "FP4_EINVAL"),
+            ("r", A + GAP + 8, "FP4_EALIGN"), ("y", A + 2 * GAP + 4, "FP4_EALIGN"),
+            ("r", A + 2 * GAP, "FP4_EOVERLAP"), ("p", A + 3 * GAP, "FP4_EOVERLAP")]
+    k, v, want = muts[int(rng.integers(len(muts)))]
+    a[k] = v
+
+    def call(lib):
+        f = lib.fp4_errfeedback_qdq
+        f.argtypes = [P, I, I64, I64, P, P, I, I, U64, U64, I, P, P, P, P]
+        return f(a["x"], a["dtype"], a["rows"], a["cols"], a["r"], a["y"], a["odt"], a["rnd"], 3, 4, a["tmode"],
+                 a["ts"], a["p"], a["s"], None)
+    return call, c[want], (k, v)
+
+
+def test_random_invalid_arguments_are_rejected(lib):
+    import numpy as np
+    c = header_constants()
+    rng = np.random.default_rng(2024)
+    makers = [lambda: _quantize_case(rng, c), lambda: _encode_case(rng, c, False),
+              lambda: _encode_case(rng, c, True), lambda: _fp8_case(rng, c), lambda: _ef_case(rng, c)]
+    for i in range(3000):
+        call, want, what = makers[i % len(makers)]()
+        got = call(lib)
+        assert got == want, (i % len(makers), what, got, want)
