@@ -19,7 +19,7 @@ sample, and a breakdown of the other operations of the codec at their own
 workload shapes.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-breakdown]
-                       [--no-cpu-baseline] [--cpu-seconds S] [--profile-mode {headline,copy,fp8col}]
+                       [--no-cpu-baseline] [--cpu-seconds S] [--profile-mode {headline,copy,fp8col,alu}]
        python bench.py --summarize-trace DIR --out FILE --command CMD
        python bench.py --summarize-pmc F_HEAD,F_COPY,W_HEAD,W_COPY --out FILE --command CMD
 """
@@ -220,6 +220,30 @@ def fp8col_probe(args, torch, fp4, synth):
     log(f"[bench] profile-mode fp8col: {args.steps} conversions")
 
 
+def alu_probe(args, torch, fp4, np, synth):
+    """The rows judged against the VALU issue rate, each launched `steps`
+    times (PMC runs): NVFP4 SR quantize of 8192x8192 bf16 with a given S_t,
+    and the FP4Quant encoders of the 8192x4096 TP tensor (RTN G=256, SR
+    G=64 and G=256)."""
+    g = torch.Generator(device="cuda").manual_seed(11)
+    x = (torch.randn((8192, 8192), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    p = torch.empty((8192, 4096), dtype=torch.uint8, device="cuda")
+    s = torch.empty((8192, 512), dtype=torch.uint8, device="cuda")
+    ts = torch.tensor([np.float32(0.03 / 2688)], dtype=torch.float32, device="cuda")
+    for k in range(args.steps):
+        fp4.fp4_quantize(x, "nvfp4", "sr", seed=1, step=k, tscale="given", tensor_scale=ts, packed=p, scales=s)
+    del x, p, s
+    tb = synth.tp_tensor()
+    xt = torch.from_numpy(tb.view(np.int16)).view(torch.bfloat16).cuda()
+    for G in (64, 256):
+        for k in range(args.steps):
+            if G == 256:
+                fp4.fp4quant_encode(xt, G)
+            fp4.fp4quant_encode_ex(xt, G, "sr", 5, k)
+    torch.cuda.synchronize()
+    log(f"[bench] profile-mode alu: {args.steps} launches of each ALU-bound row")
+
+
 # ------------------------------------------------------------ breakdown
 def breakdown(args, torch, fp4, np, synth, deferred):
     out = []
@@ -252,7 +276,10 @@ def breakdown(args, torch, fp4, np, synth, deferred):
     def nv_compute(x):
         return NV.quantize_packed(x, NV.tensor_scale(x))
 
-    def add(op, workload, nbytes, ms, note=None, oracle=None, bound="hbm", extra_bytes=0):
+    valu = read_valu_summary()
+
+    def add(op, workload, nbytes, ms, note=None, oracle=None, bound="hbm", extra_bytes=0, valu_row=None,
+            elements=None):
         """oracle: (callable returning the algorithmic bytes of one call on a
         host sample, description of the sample), timed single-threaded.
         bound: what the row is judged against (BOUNDS); extra_bytes: bytes a
@@ -266,6 +293,12 @@ def breakdown(args, torch, fp4, np, synth, deferred):
             e["two_pass_bytes"] = nbytes + extra_bytes
             e["two_pass_GBps"] = round(two, 1)
             e["frac_of_hbm_peak_two_pass"] = round(two / HBM_PEAK_GBS, 4)
+        if valu_row is not None and valu_row in valu and elements:
+            # VALU issue-bound time: instructions counted by rocprofv3 (profiles/), one
+            # wave64 instruction per CU per cycle, against this run's time
+            t_valu = valu[valu_row] * elements / 64 / (CUS * CLOCK_HZ)
+            e["valu_instructions_per_element"] = valu[valu_row]
+            e["frac_of_valu_peak"] = round(t_valu / (ms * 1e-3), 4)
         if note:
             e["note"] = note
         if with_oracle and oracle is not None:
@@ -359,7 +392,7 @@ def breakdown(args, torch, fp4, np, synth, deferred):
     add("nvfp4_quantize(sr,given)", "8192x8192 bf16", nb,
         timed(lambda k: fp4.fp4_quantize(xs[k % NS], "nvfp4", "sr", seed=1, step=k, tscale="given",
                                          tensor_scale=ts, packed=ps[k % NS], scales=ss[k % NS]), iters),
-        oracle=o_sr, bound="alu")
+        oracle=o_sr, bound="alu", valu_row="nvfp4 quantize sr, 8192x8192 bf16", elements=n)
     del xs, ps, ss, ys
 
     # MXFP4 with fp32 activations: quantize from fp32, dequantize to fp32 (4096 x 7168, 4 sets)
@@ -404,7 +437,8 @@ def breakdown(args, torch, fp4, np, synth, deferred):
                        prep=lambda xq=xq, G=G: Q.encode(xq, G) + (G,))
         add(f"fp4quant_encode(G={G})", "8192x4096 bf16 TP tensor", nb,
             timed(lambda k: fp4.fp4quant_encode(xs[k % 4], G, pk[k % 4], s1[k % 4], s2[k % 4]), iters),
-            oracle=o_e, bound="alu" if G >= 256 else "hbm")
+            oracle=o_e, bound="alu" if G >= 256 else "hbm",
+            valu_row=f"fp4quant encode rtn G={G}, 8192x4096 bf16", elements=n)
         add(f"fp4quant_decode(G={G})", "8192x4096 bf16 TP tensor", nb,
             timed(lambda k: fp4.fp4quant_decode(pk[k % 4], s1[k % 4], s2[k % 4], R, C, G, y=ys[k % 4]),
                   iters), oracle=o_de)
@@ -415,7 +449,8 @@ def breakdown(args, torch, fp4, np, synth, deferred):
         add(f"fp4quant_encode_sr(G={G})", "8192x4096 bf16 TP tensor", nb,
             timed(lambda k: fp4.fp4quant_encode_ex(xs[k % 4], G, "sr", 5, k, pk[k % 4], s1[k % 4],
                                                    s2[k % 4]), iters),
-            "stochastic-rounding variant (Philox draws per element)", oracle=o_sr, bound="alu")
+            "stochastic-rounding variant (Philox draws per element)", oracle=o_sr, bound="alu",
+            valu_row=f"fp4quant encode sr G={G}, 8192x4096 bf16", elements=n)
     del xs, pk, s1, s2, ys, x
 
     # C4: SR + error feedback step on an 8192 x 8192 weight (x fp32, r fp32, W bf16)
@@ -651,6 +686,26 @@ def host_cpus():
 
 
 # ------------------------------------------------------------ PMC summary
+VALU_SUMMARY = os.path.join(ROOT, "profiles", "valu_alu_rows_8192x8192_8192x4096.txt")
+
+
+def read_valu_summary():
+    """row label -> VALU instructions per element, from the committed counter summary."""
+    out = {}
+    if not os.path.exists(VALU_SUMMARY):
+        return out
+    for line in open(VALU_SUMMARY):
+        if line.startswith("#") or line.startswith(" ") or line.startswith("row"):
+            continue
+        parts = line.split()
+        if len(parts) < 8:
+            continue
+        label = " ".join(parts[:-7])
+        try:
+            out[label] = float(parts[-4])
+        except ValueError:
+            pass
+    return out
 def read_pmc_summary():
     if not os.path.exists(PMC_SUMMARY):
         return None
@@ -773,6 +828,61 @@ def summarize_pmc_kernel(dirs, out, command, prefix, alg, title):
     print("\n".join(lines))
 
 
+# Elements per launch of the ALU-bound rows of --profile-mode alu (by kernel
+# name prefix): 8192 x 8192 NVFP4 SR, 8192 x 4096 FP4Quant encoders.
+ALU_ROWS = [("quantize_kernel<true, false, true", "nvfp4 quantize sr, 8192x8192 bf16", 8192 * 8192),
+            ("fq_encode_rows_kernel<true, 64, true", "fp4quant encode sr G=64, 8192x4096 bf16", 8192 * 4096),
+            ("fq_encode_rows_kernel<true, 256, true", "fp4quant encode sr G=256, 8192x4096 bf16", 8192 * 4096),
+            ("fq_encode_rows_kernel<true, 256, false", "fp4quant encode rtn G=256, 8192x4096 bf16", 8192 * 4096)]
+CUS, CLOCK_HZ = 256, 2.4e9
+
+
+def summarize_valu(dirs, trace_dir, out, command):
+    """rocprofv3 --pmc runs (comma-separated output dirs) of --profile-mode alu
+    and a --kernel-trace run of the same mode -> per kernel: VALU
+    instructions per element and the VALU issue-bound time, against the
+    traced duration.  The bound: a CU issues one wave64 VALU instruction per
+    cycle (four SIMDs, four cycles each): t_valu = INSTS_VALU / (256 CUs x
+    2.4 GHz).  (SQ_ACTIVE_INST_VALU, the SIMD quad-cycles spent on VALU
+    work, equals INSTS_VALU to within 1% on these kernels, so the 64-bit
+    integer products of Philox issue at the full rate.)"""
+    import statistics
+    ctr = {}
+    for d in dirs.split(","):
+        for name, cname, v in _rocpd_rows(d, "select kernel_name, counter_name, value from counters_collection"):
+            ctr.setdefault((_short(name), cname), []).append(float(v))
+    dur = {}
+    for name, du in _rocpd_rows(trace_dir, "select name, duration from kernels"):
+        dur.setdefault(_short(name), []).append(du / 1e3)
+    lines = ["# rocprofv3 PMC summary: VALU work of the ALU-bound rows (medians per dispatch)",
+             f"# command: {command}", f"# source_digest: {source_digest()}",
+             "# t_valu = SQ_INSTS_VALU / (256 CUs x 2.4 GHz): one wave64 VALU instruction per CU per cycle",
+             "# (SQ_ACTIVE_INST_VALU, SIMD quad-cycles of VALU work, is within 1% of SQ_INSTS_VALU);",
+             "# frac = t_valu / traced median duration",
+             f"{'row':44s} {'waves':>8s} {'VALU/wave':>10s} {'INT64/wave':>10s} {'VALU/elem':>10s} "
+             f"{'t_valu us':>10s} {'traced us':>10s} {'frac':>6s}"]
+    for prefix, label, n in ALU_ROWS:
+        kn = next((k for (k, c) in ctr if k.startswith(prefix)), None)
+        if kn is None:
+            lines.append(f"{label:44s} (no counters)")
+            continue
+
+        def med(c):
+            v = ctr.get((kn, c))
+            return statistics.median(v) if v else float("nan")
+        waves, valu, i64 = med("SQ_WAVES"), med("SQ_INSTS_VALU"), med("SQ_INSTS_VALU_INT64")
+        t_valu = valu / (CUS * CLOCK_HZ) * 1e6
+        kd = next((k for k in dur if k.startswith(prefix)), None)
+        t = statistics.median(dur[kd]) if kd else float("nan")
+        lines.append(f"{label:44s} {waves:8.0f} {valu / waves:10.1f} {i64 / waves:10.1f} {valu * 64 / n:10.2f} "
+                     f"{t_valu:10.2f} {t:10.2f} {t_valu / t:6.3f}")
+        for c in ("SQ_ACTIVE_INST_VALU", "SQ_BUSY_CU_CYCLES", "SQ_INSTS_SALU", "GRBM_GUI_ACTIVE"):
+            if (kn, c) in ctr:
+                lines.append(f"    {c}: {med(c):.0f}")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -790,16 +900,21 @@ def main():
                     help="minimum oracle time for each cpu_baseline leg")
     ap.add_argument("--oracle-row-seconds", type=float, default=1.0,
                     help="minimum oracle time per breakdown row")
-    ap.add_argument("--profile-mode", choices=["headline", "copy", "fp8col"])
+    ap.add_argument("--profile-mode", choices=["headline", "copy", "fp8col", "alu"])
     ap.add_argument("--summarize-pmc", help="FETCH_headline,FETCH_copy,WRITE_headline,WRITE_copy dirs")
     ap.add_argument("--summarize-trace", help="rocprofv3 --kernel-trace output dir")
     ap.add_argument("--summarize-pmc-fp8col", help="FETCH_fp8col,FETCH_copy,WRITE_fp8col,WRITE_copy dirs")
+    ap.add_argument("--summarize-valu", help="comma-separated --pmc output dirs of --profile-mode alu")
+    ap.add_argument("--trace-dir", help="--kernel-trace output dir of the same mode (with --summarize-valu)")
     ap.add_argument("--out")
     ap.add_argument("--command", default="", help="the profiled command, recorded in the summary")
     args = ap.parse_args()
 
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc, args.out, args.command)
+        return 0
+    if args.summarize_valu:
+        summarize_valu(args.summarize_valu, args.trace_dir, args.out, args.command)
         return 0
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.out, args.command)
@@ -829,6 +944,9 @@ def main():
         return 0
     if args.profile_mode == "fp8col":
         fp8col_probe(args, torch, fp4, synth)
+        return 0
+    if args.profile_mode == "alu":
+        alu_probe(args, torch, fp4, np, synth)
         return 0
     h = headline(args, torch, fp4, np, synth)
     if args.profile_mode:
