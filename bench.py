@@ -500,6 +500,18 @@ def breakdown(args, torch, fp4, np, synth, deferred):
     add("mxfp4_row_to_fp8_col", "65536x7168, 256 Zipf(1.1) experts", nb,
         timed(lambda k: fp4.mxfp4_row_to_fp8_col(pk, sc, offd, H, o8, s8), max(iters // 2, 5)),
         oracle=o_col)
+    # the same shards with FP8 blocks of 128 tokens per channel (the token-direction reading)
+    nsc = fp4.tokblk_scale_count(T, E, H)
+    s8t = torch.empty(nsc, dtype=torch.float32, device="cuda")
+    nb_tok = T * H // 2 + T * H // 32 + T * H + 4 * H * int(sum((int(c) + 127) // 128 for c in counts))
+    o_tok = None
+    if with_oracle:
+        o_tok = leg(O8.convert_token_blocks, nb_tok * m // T,
+                    f"the first {m} tokens in their expert layout", ph8, sh8, offm, H)
+    add("mxfp4_row_to_fp8_col_tokblk", "65536x7168, 256 Zipf(1.1) experts, 128-token blocks", nb_tok,
+        timed(lambda k: fp4.mxfp4_row_to_fp8_col_tokblk(pk, sc, offd, H, o8, s8t), max(iters // 2, 5)),
+        oracle=o_tok)
+    del s8t
     # the same rows -> FP8 rows (no transpose): the dispatch receiver
     o8r, s8r = o8.view(T, H), s8.view(T, H // 128)
     add("mxfp4_row_to_fp8_row", "65536x7168", nb,

@@ -9,7 +9,8 @@ import: there is no CPU fallback.
 
 Entry points (same names as the C ABI in include/fp4mi.h):
   fp4_quantize, fp4_dequantize, fp4quant_encode, fp4quant_decode,
-  fp4_errfeedback_qdq, mxfp4_row_to_fp8_col, mxfp4_row_to_fp8_row
+  fp4_errfeedback_qdq, mxfp4_row_to_fp8_col, mxfp4_row_to_fp8_col_tokblk,
+  mxfp4_row_to_fp8_row
 plus ErrorFeedback, a name-keyed holder of residual buffers in the style of
 the fp4-train page's ErrorFeedback.qdq(name, x, step).
 """
@@ -43,6 +44,7 @@ _SIGS = {
     "fp4quant_decode": [_p, _p, _p, _i64, _i64, _i32, _p, _i, _p],
     "fp4_errfeedback_qdq": [_p, _i, _i64, _i64, _p, _p, _i, _i, _u64, _u64, _i, _p, _p, _p, _p],
     "mxfp4_row_to_fp8_col": [_p, _p, _p, _i32, _i64, _i64, _p, _p, _p],
+    "mxfp4_row_to_fp8_col_tokblk": [_p, _p, _p, _i32, _i64, _i64, _p, _p, _p],
     "mxfp4_row_to_fp8_row": [_p, _p, _i64, _i64, _p, _p, _p],
 }
 for _name, _args in _SIGS.items():
@@ -257,6 +259,36 @@ def mxfp4_row_to_fp8_col(packed, scales_e8m0, token_offsets, hidden, fp8_out=Non
     _arg(fp8_out, "fp8_out", torch.uint8, T * hidden, packed.device)
     _arg(fp8_scales, "fp8_scales", torch.float32, T * hidden // 128, packed.device)
     _check("mxfp4_row_to_fp8_col", _lib.mxfp4_row_to_fp8_col(
+        _ptr(packed), _ptr(scales_e8m0), _ptr(token_offsets), E, T, hidden, _ptr(fp8_out),
+        _ptr(fp8_scales), _stream(stream)))
+    return fp8_out, fp8_scales
+
+
+def tokblk_scale_count(total_tokens, num_experts, hidden):
+    """fp32 elements of the token-block scale buffer: H (ceil(T / 128) + E)."""
+    return hidden * ((total_tokens + 127) // 128 + num_experts)
+
+
+def mxfp4_row_to_fp8_col_tokblk(packed, scales_e8m0, token_offsets, hidden, fp8_out=None,
+                                fp8_scales=None, stream=None):
+    """Ragged MXFP4 rows [T, H/2] (+ UE8M0 [T, H/32]) -> per-expert FP8 E4M3
+    columns (flat uint8 [T*H]) with FP8 blocks of 128 tokens per channel, and
+    fp32 scales (flat [H (ceil(T/128) + E)]; expert e's [H, ceil(n_e/128)]
+    matrix at element H (ceil(off_e/128) + e))."""
+    _dev(packed)
+    T = packed.shape[0]
+    E = token_offsets.numel() - 1
+    nsc = tokblk_scale_count(T, E, hidden)
+    if fp8_out is None:
+        fp8_out = torch.empty(T * hidden, dtype=torch.uint8, device=packed.device)
+    if fp8_scales is None:
+        fp8_scales = torch.empty(nsc, dtype=torch.float32, device=packed.device)
+    _arg(packed, "packed", torch.uint8, T * hidden // 2, packed.device)
+    _arg(scales_e8m0, "scales_e8m0", torch.uint8, T * hidden // 32, packed.device)
+    _arg(token_offsets, "token_offsets", torch.int64, 1, packed.device)
+    _arg(fp8_out, "fp8_out", torch.uint8, T * hidden, packed.device)
+    _arg(fp8_scales, "fp8_scales", torch.float32, nsc, packed.device)
+    _check("mxfp4_row_to_fp8_col_tokblk", _lib.mxfp4_row_to_fp8_col_tokblk(
         _ptr(packed), _ptr(scales_e8m0), _ptr(token_offsets), E, T, hidden, _ptr(fp8_out),
         _ptr(fp8_scales), _stream(stream)))
     return fp8_out, fp8_scales

@@ -163,14 +163,18 @@ __device__ __forceinline__ int off_at(const int64_t* off, const int* offs, int T
   else return clampT(off[e], T);
 }
 
+// Padded start of expert e whose first token is o: PAD (ceil(o / PAD) + e).
+template <int PAD>
+__device__ __forceinline__ int padded_start(int o, int e) { return PAD * ((o + PAD - 1) / PAD + e); }
+
 // Expert whose padded range holds position P, by 64-way search (uniform).
-template <bool LDS_TABLE>
+template <bool LDS_TABLE, int PAD>
 __device__ int find_expert_t(const int64_t* off, const int* offs, int E, int T, int P, int lane) {
   int lo = 0, hi = E;
   while (hi - lo > 1) {
     const int step = (hi - lo + 63) / 64;
     const int e = lo + lane * step;
-    const bool le = e < hi && 16 * ((off_at<LDS_TABLE>(off, offs, T, e) + 15) / 16 + e) <= P;
+    const bool le = e < hi && padded_start<PAD>(off_at<LDS_TABLE>(off, offs, T, e), e) <= P;
     const uint64_t m = __ballot(le);
     const int last = m ? 63 - __builtin_clzll(m) : 0;
     lo += last * step;
@@ -182,17 +186,17 @@ __device__ int find_expert_t(const int64_t* off, const int* offs, int E, int T, 
 // Plan of item (tile, bp): candidate experts e_base + lane (e_base starts at
 // or before the tile), then per chunk the last candidate starting at or
 // before it.
-template <bool LDS_TABLE>
+template <bool LDS_TABLE, int PAD>
 __device__ __forceinline__ ColPlan plan_item(const int64_t* off, const int* offs, int E, int T,
                                              int tile, int bp, int lane, int q1, int g, int q2) {
   const int P0 = tile * kCTile;
-  const int eb = find_expert_t<LDS_TABLE>(off, offs, E, T, P0, lane);
+  const int eb = find_expert_t<LDS_TABLE, PAD>(off, offs, E, T, P0, lane);
   const int e = eb + lane;
   int c_off = T, c_n = 0, c_poff = 0x7FFFFFFF;
   if (e < E) {
     c_off = off_at<LDS_TABLE>(off, offs, T, e);
     c_n = max(off_at<LDS_TABLE>(off, offs, T, e + 1) - c_off, 0);
-    c_poff = 16 * ((c_off + 15) / 16 + e);
+    c_poff = padded_start<PAD>(c_off, e);
   }
   // per lane, the last candidate starting at or before each of its two chunks:
   // a binary search over the candidates' starts (ascending for ascending
@@ -251,7 +255,7 @@ __global__ __launch_bounds__(kCThreads) void fp8col_tiles_kernel(
     for (int e = tid; e <= E; e += kCThreads) offs[e] = clampT(off[e], T);
   __syncthreads();
 
-  ColPlan cur = plan_item<LDS_TABLE>(off, offs, E, T, (int)(j % ntiles), (int)(j / ntiles), lane,
+  ColPlan cur = plan_item<LDS_TABLE, 16>(off, offs, E, T, (int)(j % ntiles), (int)(j / ntiles), lane,
                                      q1, g, q2);
   ColRegs rc;
   load_item(packed, sb, cur, HB, H, s8, rc);
@@ -264,7 +268,7 @@ __global__ __launch_bounds__(kCThreads) void fp8col_tiles_kernel(
     ColPlan nxt = cur;
     ColRegs rn = rc;
     if (more) {
-      nxt = plan_item<LDS_TABLE>(off, offs, E, T, (int)(jn % ntiles), (int)(jn / ntiles), lane,
+      nxt = plan_item<LDS_TABLE, 16>(off, offs, E, T, (int)(jn % ntiles), (int)(jn / ntiles), lane,
                                  q1, g, q2);
       load_item(packed, sb, nxt, HB, H, s8, rn);
     }
@@ -353,6 +357,172 @@ int launch_fp8col_tiles(const uint8_t* packed, const uint8_t* sb, const int64_t*
                        sb, off, E, (int)T, H, (int)ntiles, nitems, ipx, (int)slots, out, sc_out);
   else
     hipLaunchKernelGGL((fp8col_tiles_kernel<false>), dim3(grid), dim3(kCThreads), 0, st, packed,
+                       sb, off, E, (int)T, H, (int)ntiles, nitems, ipx, (int)slots, out, sc_out);
+  return launch_status();
+}
+
+// ------------------------------------------- FP8 columns, blocks of 128 tokens
+// The same conversion with FP8 blocks along the tokens (the FP8 copy that
+// the backward pass contracts over the tokens): after the per-expert
+// transpose, block j of channel h is tokens 128 j .. 128 j + 127 of the
+// expert, and its target scale is the largest UE8M0 byte of those tokens for
+// the channel's 32-channel group (a partial last block uses the tokens it
+// has).  The tiles of fp8col_tiles_kernel are reused with experts padded to
+// 128 positions (expert e starts at position 128 (ceil(off_e / 128) + e)), so
+// every 128-position slot of a 512-position tile is one token block of one
+// expert or padding.  Per item:
+//   1. each loader lane takes the largest sub-block byte of its 4 tokens; a
+//      wave reduces its 8 lanes of each sub-block with shuffles and LDS
+//      max-atomics combine the 4 waves of a slot: S_tgt[slot][sub-block];
+//   2. after a barrier the values are remapped with d = S_tgt - S_sub and
+//      transposed into the LDS tile as before, and thread (slot, channel)
+//      writes the fp32 scale 2^(S_tgt - 127) of its channel and block;
+//   3. after a second barrier the rows are stored as before.
+// Expert e's scales form an [H, ceil(n_e / 128)] matrix at element
+// H (ceil(off_e / 128) + e): a closed form of the offsets, so no prefix sum.
+template <bool LDS_TABLE>
+__global__ __launch_bounds__(kCThreads) void fp8col_tokblk_kernel(
+    const uint8_t* __restrict__ packed, const uint8_t* __restrict__ sb,
+    const int64_t* __restrict__ off, int E, int T, int64_t H, int ntiles, int64_t nitems,
+    int64_t ipx, int slots, uint8_t* __restrict__ out, float* __restrict__ sc_out) {
+  __shared__ uint32_t tile[2 * 128 * kCRowDw];
+  __shared__ uint32_t lut[(kMaxShift + 1) * 2];
+  __shared__ int offs[LDS_TABLE ? kOffLds : 1];
+  __shared__ uint32_t tmax[4][8];       // S_tgt per (128-position slot, sub-block of the pair)
+  __shared__ int slot_u[4], slot_n[4];  // local index of the slot's first position, expert size
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int s8 = lane & 7, g = 8 * wave + (lane >> 3), q1 = g >> 2, q2 = lane & 31;
+  const int slot = wave >> 2;           // the loader lane's slot: positions 128 slot ..
+  const int64_t HB = H / 128;
+  const int xcd = (int)(blockIdx.x % kXcds), sl = (int)(blockIdx.x / kXcds);
+  const int64_t i0 = xcd * ipx, i1 = min(i0 + ipx, nitems);
+  int64_t j = i0 + sl;
+  if (j >= i1) return;                                  // uniform per workgroup
+  if (tid < (kMaxShift + 1) * 2) {
+    const int d = tid >> 1, hf = tid & 1;
+    uint32_t w = 0;
+    for (int k = 0; k < 4; ++k) w |= remap_e2m1_to_e4m3((uint32_t)(4 * hf + k), d) << (8 * k);
+    lut[tid] = w;
+  }
+  if (tid < 32) tmax[tid >> 3][tid & 7] = 0u;
+  if constexpr (LDS_TABLE)
+    for (int e = tid; e <= E; e += kCThreads) offs[e] = clampT(off[e], T);
+  __syncthreads();
+
+  ColPlan cur = plan_item<LDS_TABLE, 128>(off, offs, E, T, (int)(j % ntiles), (int)(j / ntiles),
+                                          lane, q1, g, q2);
+  ColRegs rc;
+  load_item(packed, sb, cur, HB, H, s8, rc);
+
+#pragma unroll 1
+  for (;;) {
+    const int64_t jn = j + slots;
+    const bool more = jn < i1;
+    ColPlan nxt = cur;
+    ColRegs rn = rc;
+    if (more) {
+      nxt = plan_item<LDS_TABLE, 128>(off, offs, E, T, (int)(jn % ntiles), (int)(jn / ntiles),
+                                      lane, q1, g, q2);
+      load_item(packed, sb, nxt, HB, H, s8, rn);
+    }
+    // 1. block targets (tokens outside the experts load byte 0, which never raises a max)
+    {
+      uint32_t m = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) m = max(m, (rc.s[k] >> (8 * (s8 & 3))) & 0xFFu);
+      m = max(m, (uint32_t)__shfl_xor((int)m, 8));
+      m = max(m, (uint32_t)__shfl_xor((int)m, 16));
+      m = max(m, (uint32_t)__shfl_xor((int)m, 32));
+      if ((lane >> 3) == 0) atomicMax(&tmax[slot][s8], m);
+      if (lane == 0 && (wave & 3) == 0) {
+        slot_u[slot] = cur.u1;
+        slot_n[slot] = cur.n1;
+      }
+    }
+    lds_barrier();
+    // 2. remap, transpose, LDS; scales
+    {
+      const uint32_t s_tgt = tmax[slot][s8];
+      uint32_t ev[4][4], od[4][4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t s_sub = (rc.s[k] >> (8 * (s8 & 3))) & 0xFFu;
+        const int d = min((int)(s_tgt - s_sub), kMaxShift);
+        const uint32_t tlo = lut[2 * d], thi = lut[2 * d + 1];
+        const uint32_t ww[4] = {rc.w[k].x, rc.w[k].y, rc.w[k].z, rc.w[k].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t w = ww[i];
+          ev[k][i] = __builtin_amdgcn_perm(thi, tlo, w & 0x07070707u) | ((w << 4) & 0x80808080u);
+          od[k][i] = __builtin_amdgcn_perm(thi, tlo, (w >> 4) & 0x07070707u) | (w & 0x80808080u);
+        }
+      }
+      uint32_t* row0 = tile + 32 * s8 * kCRowDw + (g ^ col_swz(s8));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t y[8];
+        transpose4x4(ev[0][i], ev[1][i], ev[2][i], ev[3][i], y[0], y[2], y[4], y[6]);
+        transpose4x4(od[0][i], od[1][i], od[2][i], od[3][i], y[1], y[3], y[5], y[7]);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) row0[(8 * i + c) * kCRowDw] = y[c];
+      }
+      // thread (slot ts, channel c of the pair): fp32 scale of channel 256 bp + c, block u / 128
+      const int ts = tid >> 8, c = tid & 255;
+      const int u = slot_u[ts], n = slot_n[ts];
+      const int64_t h = 256 * (int64_t)cur.bp + c;
+      if (h < H && u >= 0 && u < n) {
+        const int64_t P = (int64_t)(j % ntiles) * kCTile + 128 * ts;   // the slot's first position
+        const int64_t nb = (n + 127) / 128;
+        sc_out[H * ((P - u) / 128) + h * nb + u / 128] =
+            __builtin_amdgcn_ldexpf(1.0f, (int)tmax[ts][c >> 5] - 127);
+      }
+    }
+    lds_barrier();
+    // 3. rows 16 wave .. 16 wave + 15, one 16-byte chunk per lane
+    {
+      if (tid < 32) tmax[tid >> 3][tid & 7] = 0u;       // for the next item (read before the barrier)
+      const bool blk_ok = 2 * (int64_t)cur.bp + (wave >> 3) < HB;
+      const int L = (blk_ok && cur.u2 >= 0) ? min(max(cur.n2 - cur.u2, 0), 16) : 0;
+      const int64_t rowbase = H * (int64_t)cur.off2 + cur.u2;
+      const uint32_t* src = tile + (16 * wave + (lane >> 5)) * kCRowDw +
+                            ((4 * q2) ^ col_swz(wave >> 1));
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(src + 2 * k * kCRowDw);
+        const int64_t h = 256 * (int64_t)cur.bp + 16 * wave + 2 * k + (lane >> 5);
+        uint8_t* dst = out + rowbase + h * cur.n2;
+        if (L == 16) *reinterpret_cast<u32x4_ua*>(dst) = v;
+        else if (L > 0) store_partial(dst, v, L);
+      }
+    }
+    if (!more) break;
+    lds_barrier();
+    j = jn;
+    cur = nxt;
+    rc = rn;
+  }
+}
+
+// Items and workgroups of the token-block kernel: the tiles kernel's, over
+// 128 (ceil(T / 128) + E) padded positions.
+int launch_fp8col_tokblk(const uint8_t* packed, const uint8_t* sb, const int64_t* off, int E,
+                         int64_t T, int64_t H, uint8_t* out, float* sc_out, hipStream_t st) {
+  const int64_t ptot = 128 * ((T + 127) / 128 + (int64_t)E);
+  const int64_t ntiles = (ptot + kCTile - 1) / kCTile;
+  const int64_t npairs = (H / 128 + 1) / 2;
+  const int64_t nitems = ntiles * npairs;
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int64_t ipx = (nitems + kXcds - 1) / kXcds;
+  int64_t slots = max((int64_t)(max(cus, 1) / kXcds), (int64_t)1);
+  if (slots > ipx) slots = ipx;
+  const unsigned grid = (unsigned)(kXcds * slots);
+  if (E + 1 <= kOffLds)
+    hipLaunchKernelGGL((fp8col_tokblk_kernel<true>), dim3(grid), dim3(kCThreads), 0, st, packed,
+                       sb, off, E, (int)T, H, (int)ntiles, nitems, ipx, (int)slots, out, sc_out);
+  else
+    hipLaunchKernelGGL((fp8col_tokblk_kernel<false>), dim3(grid), dim3(kCThreads), 0, st, packed,
                        sb, off, E, (int)T, H, (int)ntiles, nitems, ipx, (int)slots, out, sc_out);
   return launch_status();
 }
@@ -452,6 +622,38 @@ extern "C" int mxfp4_row_to_fp8_col(const uint8_t* packed, const uint8_t* scales
   clear_stale_error();
   return launch_fp8col_tiles(packed, scales_e8m0, token_offsets, num_experts, total_tokens,
                              hidden, fp8_out, fp8_scales, as_stream(stream));
+}
+
+extern "C" int mxfp4_row_to_fp8_col_tokblk(const uint8_t* packed, const uint8_t* scales_e8m0,
+                                           const int64_t* token_offsets, int32_t num_experts,
+                                           int64_t total_tokens, int64_t hidden, uint8_t* fp8_out,
+                                           float* fp8_scales, void* stream) {
+  if (num_experts < 1) return FP4_EINVAL;
+  if (total_tokens < 0 || hidden <= 0 || hidden % 128) return FP4_ESHAPE;
+  // padded positions (< 128 (T / 128 + E + 2)) stay in int32
+  if (total_tokens >= (int64_t(1) << 26) || hidden >= (int64_t(1) << 21) ||
+      num_experts >= (1 << 23))
+    return FP4_ESHAPE;
+  int64_t n;
+  if (!checked_count(total_tokens, hidden, &n)) return FP4_ESHAPE;
+  if (!token_offsets) return FP4_EINVAL;
+  if (n == 0) return FP4_OK;
+  if (!packed || !scales_e8m0 || !fp8_out || !fp8_scales) return FP4_EINVAL;
+  if (!is_aligned(packed, 16) || !is_aligned(scales_e8m0, 4) || !is_aligned(token_offsets, 8) ||
+      !is_aligned(fp8_out, 4) || !is_aligned(fp8_scales, 4))
+    return FP4_EALIGN;
+  const int64_t pb = n / 2, sbb = n / 32, ob = n,
+                scb = hidden * ((total_tokens + 127) / 128 + num_experts) * 4,
+                offb = ((int64_t)num_experts + 1) * 8;
+  const void* ins[3] = {packed, scales_e8m0, token_offsets};
+  const int64_t inn[3] = {pb, sbb, offb};
+  for (int k = 0; k < 3; ++k)
+    if (overlaps(fp8_out, ob, ins[k], inn[k]) || overlaps(fp8_scales, scb, ins[k], inn[k]))
+      return FP4_EOVERLAP;
+  if (overlaps(fp8_out, ob, fp8_scales, scb)) return FP4_EOVERLAP;
+  clear_stale_error();
+  return launch_fp8col_tokblk(packed, scales_e8m0, token_offsets, num_experts, total_tokens,
+                              hidden, fp8_out, fp8_scales, as_stream(stream));
 }
 
 extern "C" int mxfp4_row_to_fp8_row(const uint8_t* packed, const uint8_t* scales_e8m0,

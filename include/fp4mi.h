@@ -219,6 +219,35 @@ int mxfp4_row_to_fp8_col(const uint8_t* packed, const uint8_t* scales_e8m0,
                          uint8_t* fp8_out, float* fp8_scales, void* stream);
 
 /*
+ * mxfp4_row_to_fp8_col_tokblk -- the fused MXFP4-row -> FP8-E4M3-column
+ * conversion with FP8 blocks along the tokens: the FP8 copy that feeds the
+ * backward pass, whose weight gradient contracts over the tokens (MoE report
+ * "Practical FP4 Training for Large-Scale MoE Models on Hopper GPUs",
+ * section "核心技术贡献" items 1-3; section "方法概述": the backward pass stays
+ * in FP8).  After the per-expert transpose to [H, n_e], block j of channel h
+ * is the expert's tokens 128j .. 128j+127 (the last block of a shard may be
+ * partial), and its target scale is the largest source scale of the block:
+ *   S_tgt(h, j) = max over the block's tokens t of UE8M0[t, h/32];
+ *   out[h, t-off[e]] = E4M3_RNE_sat(e2m1(code[t,h]) * 2^-(S_tgt - UE8M0[t, h/32]));
+ *   scale[h, j] = 2^(S_tgt - 127) (fp32).
+ *
+ *  packed, scales_e8m0, token_offsets, hidden, fp8_out: as mxfp4_row_to_fp8_col
+ *  num_experts    1 <= E < 2^23 (FP4_EINVAL below 1, FP4_ESHAPE from 2^23);
+ *                 total_tokens 0 <= T < 2^26;  hidden 0 < H < 2^21, H % 128 == 0
+ *  fp8_scales     out fp32 [H * (ceil(T/128) + E)], 4-byte aligned; expert e's
+ *                 [H, ceil(n_e/128)] matrix starts at element
+ *                 H * (ceil(off[e]/128) + e) (a closed form of the offsets;
+ *                 the matrices never overlap; elements between them are not
+ *                 written)
+ * Outputs must not overlap inputs or each other (FP4_EOVERLAP).  Malformed
+ * offsets are clamped on the device as for mxfp4_row_to_fp8_col.
+ */
+int mxfp4_row_to_fp8_col_tokblk(const uint8_t* packed, const uint8_t* scales_e8m0,
+                                const int64_t* token_offsets, int32_t num_experts,
+                                int64_t total_tokens, int64_t hidden,
+                                uint8_t* fp8_out, float* fp8_scales, void* stream);
+
+/*
  * mxfp4_row_to_fp8_row -- MXFP4 rows -> FP8 E4M3 rows, no transpose: the
  * forward receiver that the MoE report names FP4RowToFP8Row beside
  * FP4RowToFP8Col ("Practical FP4 Training for Large-Scale MoE Models on

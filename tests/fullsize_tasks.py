@@ -229,6 +229,41 @@ def fp8col_windows(t):
     return res
 
 
+def fp8col_tokblk_windows(t):
+    """Token windows (starting on multiples of 128 tokens) of expert shards
+    for the token-block FP8 columns: window (e, u0, u1) converted by the
+    oracle as a shard of its own (a 128-token block depends only on its own
+    tokens) against columns u0 .. u1 - 1 of the library's [H, n_e] matrix and
+    columns u0/128 .. of expert e's [H, ceil(n_e/128)] scale matrix."""
+    H = t["H"]
+    off = np.asarray(t["off"], np.int64)
+    base = fp8col.token_block_scale_offset(off, H)
+    out = np.load(t["o"], mmap_mode="r")
+    sc = np.load(t["sc"], mmap_mode="r")
+    packed = np.load(t["p"], mmap_mode="r")
+    sb = np.load(t["s"], mmap_mode="r")
+    res = {"n": 0, "fp8": 0, "fp8_at": None, "scale": 0, "scale_at": None}
+    for e, u0, u1 in t["windows"]:
+        assert u0 % 128 == 0
+        a, n = int(off[e]), int(off[e + 1] - off[e])
+        w, nb = u1 - u0, (n + 127) // 128
+        ro, rs, _ = fp8col.convert_token_blocks(np.array(packed[a + u0:a + u1]), np.array(sb[a + u0:a + u1]),
+                                                np.array([0, w], np.int64), H)
+        got = np.array(out[H * a:H * (a + n)]).reshape(H, n)[:, u0:u1]
+        k, at = _diff(got, ro.reshape(H, w))
+        if k:
+            res["fp8"] += k
+            res["fp8_at"] = res["fp8_at"] or (e, at[0], at[1] + u0)
+        wb = (w + 127) // 128
+        gs = np.array(sc[base[e]:base[e] + H * nb]).reshape(H, nb)[:, u0 // 128:u0 // 128 + wb]
+        k, at = _diff(gs, rs[:H * wb].reshape(H, wb))
+        if k:
+            res["scale"] += k
+            res["scale_at"] = res["scale_at"] or (e, at[0], at[1] + u0 // 128)
+        res["n"] += H * w
+    return res
+
+
 def fp8row_rows(t):
     """Tokens [a, b) of the FP8 row receiver against the oracle."""
     a, b, H = t["a"], t["b"], t["H"]

@@ -133,6 +133,26 @@ def test_other_entry_points_validation(lib):
     assert dq(A, A + (1 << 30), None, 4, 64, 0, A + (3 << 30), 1, None) == c["FP4_EINVAL"]
 
 
+def test_fp8_tokblk_validation(lib):
+    c = header_constants()
+    f = lib.mxfp4_row_to_fp8_col_tokblk
+    f.argtypes = [P, P, P, I32, I64, I64, P, P, P]
+
+    def call(packed=A, sb=A + (1 << 30), off=A + (2 << 30), E=4, T=64, H=256, out=A + (3 << 30),
+             sc=A + (4 << 30)):
+        return f(packed, sb, off, E, T, H, out, sc, None)
+
+    assert call(E=0) == c["FP4_EINVAL"]
+    assert call(H=200) == c["FP4_ESHAPE"]
+    assert call(E=1 << 23) == c["FP4_ESHAPE"]                 # experts limited to 2^23 - 1
+    assert call(T=1 << 26) == c["FP4_ESHAPE"]
+    assert call(T=0) == c["FP4_OK"]
+    assert call(off=None) == c["FP4_EINVAL"]
+    assert call(packed=A + 4) == c["FP4_EALIGN"]
+    # the scale buffer holds H (ceil(T/128) + E) floats: 256 * (1 + 4) * 4 bytes here
+    assert call(out=A + (4 << 30) + 256 * 5 * 4 - 4) == c["FP4_EOVERLAP"]
+
+
 def test_fp8_row_validation(lib):
     c = header_constants()
     f = lib.mxfp4_row_to_fp8_row
@@ -261,6 +281,27 @@ def _fp8_case(rng, c):
     return call, c[want], (k, v)
 
 
+def _fp8_tokblk_case(rng, c):
+    T, H, E = int(rng.integers(1, 1 << 20)), 128 * int(rng.integers(1, 64)), int(rng.integers(1, 1 << 12))
+    a = dict(p=A, s=A + GAP, off=A + 2 * GAP, E=E, T=T, H=H, o=A + 3 * GAP, sc=A + 4 * GAP)
+    nsc = 4 * H * ((T + 127) // 128 + E)                       # bytes of the token-block scales
+    muts = [("E", int(rng.choice([0, -1])), "FP4_EINVAL"), ("E", 1 << 23, "FP4_ESHAPE"),
+            ("T", -1, "FP4_ESHAPE"), ("T", 1 << 26, "FP4_ESHAPE"), ("H", H + 64, "FP4_ESHAPE"),
+            ("H", 0, "FP4_ESHAPE"), ("H", 1 << 21, "FP4_ESHAPE"), ("off", None, "FP4_EINVAL"),
+            ("o", None, "FP4_EINVAL"), ("sc", None, "FP4_EINVAL"), ("s", A + GAP + 2, "FP4_EALIGN"),
+            ("sc", A + 4 * GAP + 2, "FP4_EALIGN"), ("o", A + GAP, "FP4_EOVERLAP"),
+            ("sc", A + 3 * GAP + T * H - 4, "FP4_EOVERLAP"),
+            ("o", A + 4 * GAP + nsc - 4, "FP4_EOVERLAP")]       # FP8 bytes inside the last scales
+    k, v, want = muts[int(rng.integers(len(muts)))]
+    a[k] = v
+
+    def call(lib):
+        f = lib.mxfp4_row_to_fp8_col_tokblk
+        f.argtypes = [P, P, P, I32, I64, I64, P, P, P]
+        return f(a["p"], a["s"], a["off"], a["E"], a["T"], a["H"], a["o"], a["sc"], None)
+    return call, c[want], (k, v)
+
+
 def _ef_case(rng, c):
     a = dict(x=A, dtype=int(rng.integers(2)), rows=int(rng.integers(1, 1 << 20)), cols=16 * int(rng.integers(1, 512)),
              r=A + GAP, y=A + 2 * GAP, odt=int(rng.integers(2)), rnd=int(rng.integers(2)), tmode=int(rng.integers(2)),
@@ -286,7 +327,8 @@ def test_random_invalid_arguments_are_rejected(lib):
     c = header_constants()
     rng = np.random.default_rng(2024)
     makers = [lambda: _quantize_case(rng, c), lambda: _encode_case(rng, c, False),
-              lambda: _encode_case(rng, c, True), lambda: _fp8_case(rng, c), lambda: _ef_case(rng, c)]
+              lambda: _encode_case(rng, c, True), lambda: _fp8_case(rng, c), lambda: _ef_case(rng, c),
+              lambda: _fp8_tokblk_case(rng, c)]
     for i in range(3000):
         call, want, what = makers[i % len(makers)]()
         got = call(lib)

@@ -4,7 +4,11 @@ well-formed and malformed token offsets: every load of codes and scales and
 every store of FP8 bytes and fp32 scales must stay inside its buffer.  The
 model follows the kernel's integer steps: padded starts 16 (ceil(off / 16) +
 e) of clamped offsets, a 64-way search per tile, 64 candidate experts, a
-binary search for the last candidate at or before each 16-position chunk."""
+binary search for the last candidate at or before each 16-position chunk.
+The token-block variant (mxfp4_row_to_fp8_col_tokblk) runs the same
+arithmetic with padded starts 128 (ceil(off / 128) + e) and writes one fp32
+scale per (channel, 128-position slot) at H (ceil(off / 128) + e) + h
+ceil(n / 128) + u / 128."""
 import numpy as np
 import pytest
 
@@ -16,41 +20,44 @@ def clampT(v, T):
     return np.minimum(np.maximum(v, 0), T)
 
 
-def poff(offc, e):
-    return 16 * ((offc[e] + 15) // 16 + e)
+def poff(offc, e, pad=16):
+    return pad * ((offc[e] + pad - 1) // pad + e)
 
 
-def find_expert(offc, E, P):
+def find_expert(offc, E, P, pad=16):
     lo, hi = 0, E
     while hi - lo > 1:
         step = (hi - lo + 63) // 64
         e = lo + np.arange(64) * step
         ok = e < hi
         le = np.zeros(64, bool)
-        le[ok] = poff(offc, e[ok]) <= P
+        le[ok] = poff(offc, e[ok], pad) <= P
         last = int(np.nonzero(le)[0].max()) if le.any() else 0
         lo += last * step
         hi = min(lo + step, hi)
     return lo
 
 
-def check_bounds(off, T, H):
+def check_bounds(off, T, H, pad=16):
+    tokblk = pad == 128
     E = len(off) - 1
     offc = clampT(np.asarray(off, np.int64), T)
-    ptot = 16 * ((T + 15) // 16 + E)
+    ptot = pad * ((T + pad - 1) // pad + E)
     ntiles = (ptot + TILE - 1) // TILE
     HB = H // 128
     npairs = (HB + 1) // 2
-    code_bytes, scale_bytes, out_bytes, sc_floats = T * H // 2, T * H // 32, T * H, T * H // 128
+    code_bytes, scale_bytes, out_bytes = T * H // 2, T * H // 32, T * H
+    sc_floats = H * ((T + 127) // 128 + E) if tokblk else T * H // 128
+    assert ptot < 2**31
     lane = np.arange(64)
     for tile in range(ntiles):
         P0 = tile * TILE
-        eb = find_expert(offc, E, P0)
+        eb = find_expert(offc, E, P0, pad)
         e = eb + lane
         ok = e < E
         c_off = np.where(ok, offc[np.minimum(e, E - 1)], T)
         c_n = np.where(ok, np.maximum(offc[np.minimum(e + 1, E)] - c_off, 0), 0)
-        c_poff = np.where(ok, 16 * ((c_off + 15) // 16 + e), 2**31 - 1)
+        c_poff = np.where(ok, pad * ((c_off + pad - 1) // pad + e), 2**31 - 1)
         idx = np.zeros(CHUNKS, np.int64)          # binary search over the 64 candidates
         for q in range(CHUNKS):
             i, thr = 0, P0 + 16 * q
@@ -74,10 +81,23 @@ def check_bounds(off, T, H):
                     assert np.all(~val | ((a >= 0) & (a + 16 <= code_bytes)))
                     a = t * (H // 32) + 4 * b
                     assert np.all(~val | ((a >= 0) & (a + 4 <= scale_bytes)))
-                u = u1 + (s8 & 3)
-                val = (b < HB) & (u >= 0) & (u < n1)
-                a = HB * off1 + b * n1 + u
-                assert np.all(~val | ((a >= 0) & (a < sc_floats)))
+                if not tokblk:
+                    u = u1 + (s8 & 3)
+                    val = (b < HB) & (u >= 0) & (u < n1)
+                    a = HB * off1 + b * n1 + u
+                    assert np.all(~val | ((a >= 0) & (a < sc_floats)))
+                if tokblk and wave == 0:
+                    # scale of channel 256 bp + c for slot ts: thread (ts, c)
+                    for ts in range(4):
+                        i = idx[8 * ts]
+                        u, n = P0 + 128 * ts - c_poff[i], c_n[i]
+                        if not (0 <= u < n):
+                            continue
+                        h = 256 * bp + np.arange(256)
+                        h = h[h < H]
+                        nb = (n + 127) // 128
+                        a = H * ((P0 + 128 * ts - u) // 128) + h * nb + u // 128
+                        assert np.all((a >= 0) & (a < sc_floats)), (tile, ts)
                 q2 = lane & 31
                 i2 = idx[q2]
                 off2, n2 = c_off[i2], c_n[i2]
@@ -100,15 +120,17 @@ MALFORMED = [
 
 @pytest.mark.parametrize("off", MALFORMED + [[0, 3, 3, 200, 513, 600]])
 @pytest.mark.parametrize("H", [128, 384])
-def test_accesses_stay_in_bounds(off, H):
-    check_bounds(np.array(off, np.int64), 600, H)
+@pytest.mark.parametrize("pad", [16, 128])
+def test_accesses_stay_in_bounds(off, H, pad):
+    check_bounds(np.array(off, np.int64), 600, H, pad)
 
 
 def test_many_experts_and_seams():
     rng = np.random.default_rng(1)
     counts = rng.integers(0, 9, size=300)
     off = np.concatenate([[0], np.cumsum(counts)])
-    check_bounds(off, int(off[-1]), 256)
-    off2 = off.copy()
-    rng.shuffle(off2[1:-1])                 # non-monotone interior
-    check_bounds(off2, int(off[-1]), 256)
+    for pad in (16, 128):
+        check_bounds(off, int(off[-1]), 256, pad)
+        off2 = off.copy()
+        rng.shuffle(off2[1:-1])             # non-monotone interior
+        check_bounds(off2, int(off[-1]), 256, pad)

@@ -284,6 +284,27 @@ def _check_fp8col(m, pool, pp, sp, off, H, name):
     _report(name, res, ["fp8", "scale"])
 
 
+def _check_fp8col_tokblk(m, pool, pp, sp, off, H, name):
+    Tn, E = int(off[-1]), off.size - 1
+    nsc = m.tokblk_scale_count(Tn, E, H)
+    packed, sb = np.load(pp), np.load(sp)
+    go, gs = Guarded(Tn * H), Guarded(nsc * 4)
+    o, s = m.mxfp4_row_to_fp8_col_tokblk(dev_u8(packed), dev_u8(sb), dev_i64(off), H,
+                                         go.view(torch.uint8, (Tn * H,)), gs.view(torch.float32, (nsc,)))
+    torch.cuda.synchronize()
+    go.check()
+    gs.check()
+    del packed, sb
+    op, sp2 = pool.put("fp8t", host(o)), pool.put("fp8ts", host(s))
+    del o, s, go, gs
+    wins = _expert_windows(off)
+    chunks = [wins[i::4 * pool.n] for i in range(4 * pool.n)]
+    res = pool.map(T.fp8col_tokblk_windows, [dict(p=pp, s=sp, o=op, sc=sp2, off=off.tolist(), H=H, windows=c)
+                                             for c in chunks if c])
+    pool.drop(op, sp2)
+    _report(name, res, ["fp8", "scale"])
+
+
 def _check_fp8row(m, pool, pp, sp, Tn, H, name):
     packed, sb = np.load(pp), np.load(sp)
     o, s = m.mxfp4_row_to_fp8_row(dev_u8(packed), dev_u8(sb), H)
@@ -306,6 +327,7 @@ def test_fp8_receivers_zipf_shards_whole_output(pool):
     counts, off = synth.expert_counts(Tn, E, seed=5)
     pp, sp = _fp8_inputs_from_activations(pool, Tn, H)
     _check_fp8col(m, pool, pp, sp, off, H, "fp8 columns 65536x7168, 256 Zipf experts")
+    _check_fp8col_tokblk(m, pool, pp, sp, off, H, "fp8 columns, 128-token blocks, 65536x7168, 256 Zipf experts")
     _check_fp8row(m, pool, pp, sp, Tn, H, "fp8 rows 65536x7168")
     pool.drop(pp, sp)
 
@@ -321,5 +343,6 @@ def test_fp8_receivers_random_rows_whole_output(pool):
     pp, sp = pool.put("mx_p", packed), pool.put("mx_s", sb)
     del packed, sb
     _check_fp8col(m, pool, pp, sp, off, H, "fp8 columns 65536x7168 random rows")
+    _check_fp8col_tokblk(m, pool, pp, sp, off, H, "fp8 columns, 128-token blocks, 65536x7168 random rows")
     _check_fp8row(m, pool, pp, sp, Tn, H, "fp8 rows 65536x7168 random rows")
     pool.drop(pp, sp)
