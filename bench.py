@@ -34,7 +34,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "FP4 quantize+pack / dequant throughput, GB/s and % of MI355X HBM peak"
 HBM_PEAK_GBS = 8000.0
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_mxfp4_quantize_4096x7168.txt")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_mxfp4_codec_4096x7168.txt")
 KERNEL_SOURCES = ["block_scaled_fp4_amd/csrc/quant.hip", "block_scaled_fp4_amd/csrc/device_common.hpp"]
 
 
@@ -214,10 +214,12 @@ def fp8col_probe(args, torch, fp4, synth):
     offd = torch.from_numpy(off).cuda()
     o8 = torch.empty(T * H, dtype=torch.uint8, device="cuda")
     s8 = torch.empty(T * H // 128, dtype=torch.float32, device="cuda")
+    s8t = torch.empty(fp4.tokblk_scale_count(T, E, H), dtype=torch.float32, device="cuda")
     for _ in range(args.steps):
         fp4.mxfp4_row_to_fp8_col(pk, sc, offd, H, o8, s8)
+        fp4.mxfp4_row_to_fp8_col_tokblk(pk, sc, offd, H, o8, s8t)
     torch.cuda.synchronize()
-    log(f"[bench] profile-mode fp8col: {args.steps} conversions")
+    log(f"[bench] profile-mode fp8col: {args.steps} conversions of each FP8-column layout")
 
 
 def alu_probe(args, torch, fp4, np, synth):
@@ -800,11 +802,11 @@ def summarize_pmc(dirs, out, command):
              f"# copy calibration: FETCH_SIZE reads {f_copy:.0f} B for a {copy_bytes} B copy (x{kf:.4f}); "
              f"WRITE_SIZE writes {w_copy:.0f} B (x{kw:.4f})",
              f"source_digest: {source_digest()}",
-             "kernel: quantize",
+             "kernels: quantize dequantize",
              f"fetch_factor: {kf:.6f}", f"write_factor: {kw:.6f}",
-             f"quantize_fetch_bytes: {fetch[q] * kf:.0f}", f"quantize_write_bytes: {write[q] * kw:.0f}",
-             f"hbm_bytes_per_launch: {fetch[q] * kf + write[q] * kw:.0f}",
              f"algorithmic_bytes_per_launch: {alg}",
+             f"quantize_fetch_bytes: {fetch[q] * kf:.0f}", f"quantize_write_bytes: {write[q] * kw:.0f}",
+             f"quantize_hbm_bytes_per_launch: {fetch[q] * kf + write[q] * kw:.0f}",
              f"dequantize_fetch_bytes: {fetch[d] * kf:.0f}", f"dequantize_write_bytes: {write[d] * kw:.0f}",
              f"dequantize_hbm_bytes_per_launch: {fetch[d] * kf + write[d] * kw:.0f}"]
     open(out, "w").write("\n".join(lines) + "\n")
@@ -932,10 +934,19 @@ def main():
         summarize_trace(args.summarize_trace, args.out, args.command)
         return 0
     if args.summarize_pmc_fp8col:
-        T, H = 65536, 7168
+        sys.path.insert(0, ROOT)
+        import synth
+        T, H, E = 65536, 7168, 256
+        counts, _ = synth.expert_counts(T, E, seed=5)
+        base, ext = os.path.splitext(args.out)
         summarize_pmc_kernel(args.summarize_pmc_fp8col, args.out, args.command, "fp8col_tiles_kernel",
                              T * H // 2 + T * H // 32 + T * H + 4 * (T * H // 128),
                              "the MXFP4 -> FP8 column kernel (65536x7168, 256 Zipf(1.1) experts)")
+        summarize_pmc_kernel(args.summarize_pmc_fp8col, base + "_tokblk" + ext, args.command,
+                             "fp8col_tokblk_kernel",
+                             T * H // 2 + T * H // 32 + T * H + 4 * H * sum((int(c) + 127) // 128 for c in counts),
+                             "the MXFP4 -> FP8 column kernel with 128-token blocks (65536x7168, 256 Zipf(1.1) "
+                             "experts)")
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -971,9 +982,9 @@ def main():
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     traffic = None
     pmc = read_pmc_summary()
-    if pmc and pmc.get("source_digest") == source_digest() and pmc.get("kernel") == dom:
+    if pmc and pmc.get("source_digest") == source_digest() and dom in pmc.get("kernels", "").split():
         try:
-            traffic = float(pmc["hbm_bytes_per_launch"])
+            traffic = float(pmc[f"{dom}_hbm_bytes_per_launch"])
         except (KeyError, ValueError):
             traffic = None
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
