@@ -892,7 +892,13 @@ extern "C" int fp4_dequantize(const uint8_t* packed, const uint8_t* scales,
   const dim3 g((unsigned)blocks_for(n_oct, U));
   const uint32_t* pk = reinterpret_cast<const uint32_t*>(packed);
   if (out_dtype == FP4_DTYPE_BF16) {
-    if (mx) hipLaunchKernelGGL((dequantize_kernel<true, U>), dim3(g), dim3(kThreads), 0, st, pk, scales, tensor_scale, n_oct, y);
+    // MXFP4 to bf16: eight octets per thread, all eight code loads issued
+    // before the first store.  With codes resident in HBM (4096 x 7168,
+    // inputs rotating over 546 MB) this measured 13.2 us against 14.0 us
+    // with two octets per thread; with codes still in the Infinity Cache two
+    // octets are faster (11.6 us against 12.5 us).
+    constexpr int UM = 8;
+    if (mx) hipLaunchKernelGGL((dequantize_kernel<true, UM>), dim3((unsigned)blocks_for(n_oct, UM)), dim3(kThreads), 0, st, pk, scales, tensor_scale, n_oct, y);
     else    hipLaunchKernelGGL((dequantize_kernel<false, U>), dim3(g), dim3(kThreads), 0, st, pk, scales, tensor_scale, n_oct, y);
   } else {
     const int64_t n_quad = 2 * n_oct;
