@@ -774,8 +774,11 @@ void launch_quantize_t(bool sr, const void* x, int64_t n_oct, const float* ts, u
     hipLaunchKernelGGL((quantize_kernel<BF16, MX, true>), g, dim3(kThreads), 0, st, x, n_oct,
                        ts, seed, step, packed, scales);
   else if (MX)
-    hipLaunchKernelGGL((quantize_kernel<BF16, true, false>), g, dim3(kThreads), 0, st, x,
-                       n_oct, ts, seed, step, packed, scales);
+    // three octets per thread from bf16 (four from fp32): measured 1% faster
+    // than four on 4096 x 7168, with the input in HBM or in the Infinity Cache
+    hipLaunchKernelGGL((quantize_kernel<BF16, true, false, BF16 ? 3 : kOctets<BF16>>),
+                       dim3((unsigned)blocks_for(n_oct, BF16 ? 3 : kOctets<BF16>)), dim3(kThreads), 0, st,
+                       x, n_oct, ts, seed, step, packed, scales);
   else if constexpr (!BF16)
     hipLaunchKernelGGL((nv_rtn_quantize_f32_kernel<2>), dim3((unsigned)blocks_for(2 * n_oct, 2)),
                        dim3(kThreads), 0, st, static_cast<const float*>(x), 2 * n_oct, ts,
