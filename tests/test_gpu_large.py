@@ -81,7 +81,8 @@ def test_nvfp4_sr_counters_past_2_34_elements():
 
 def test_fp8_rows_and_columns_past_2_32_output_bytes():
     """655,360 tokens x 7168 in 256 Zipf(1.1) experts: 4.7 GB of FP8 output,
-    so the late experts' rows sit past byte 2^32."""
+    so the late experts' rows sit past byte 2^32; columns with FP8 blocks of
+    128 channels and of 128 tokens, and rows."""
     import synth
     from oracle import fp8col
     m = need_gpu()
@@ -120,6 +121,31 @@ def test_fp8_rows_and_columns_past_2_32_output_bytes():
             np.testing.assert_array_equal(host(orow[a + t0:a + t0 + k]), qo)
             np.testing.assert_array_equal(host(srow[a + t0:a + t0 + k]).view(np.uint32),
                                           qs.view(np.uint32))
+    # the same shards with FP8 blocks of 128 tokens, into the same FP8 buffer
+    del orow, srow
+    st = torch.empty(m.tokblk_scale_count(T, E, H), dtype=torch.float32, device="cuda")
+    m.mxfp4_row_to_fp8_col_tokblk(packed, sb, off_d, H, o, st)
+    torch.cuda.synchronize()
+    base = fp8col.token_block_scale_offset(off, H)
+    for e in (0, E // 2, E - 4, E - 2, E - 1):
+        a, b = int(off[e]), int(off[e + 1])
+        n = b - a
+        if n == 0:
+            continue
+        nb = (n + 127) // 128
+        # windows starting on 128-token blocks (a block depends only on its tokens)
+        wins = sorted({(0, min(n, 512)), (128 * max(0, (n // 2 - 256) // 128), min(n, 128 * max(0, (n // 2 - 256) // 128) + 512)),
+                       (128 * max(0, (n - 512) // 128), n)})
+        for t0, t1 in wins:
+            pk, sc = host(packed[a + t0:a + t1]), host(sb[a + t0:a + t1])
+            wb = (t1 - t0 + 127) // 128
+            for blk in (0, HB - 1):
+                cols, scs = slice(blk * 64, blk * 64 + 64), slice(blk * 4, blk * 4 + 4)
+                ro, rs, _ = fp8col.convert_token_blocks(pk[:, cols], sc[:, scs], np.array([0, t1 - t0], np.int64), 128)
+                rows = o[H * a: H * b].view(H, n)[blk * 128: blk * 128 + 128, t0:t1]
+                np.testing.assert_array_equal(host(rows).reshape(-1), ro)
+                gs = st[int(base[e]): int(base[e]) + H * nb].view(H, nb)[blk * 128: blk * 128 + 128, t0 // 128: t0 // 128 + wb]
+                np.testing.assert_array_equal(host(gs).view(np.uint32), rs[:128 * wb].reshape(128, wb).view(np.uint32))
 
 
 def test_errfeedback_past_2_32_elements():
