@@ -14,7 +14,11 @@ pytestmark = pytest.mark.gpu
 
 def _replay_check(fn, outs, replays=4):
     """fn() writes into the tensors `outs`; eager result first, then a captured
-    graph replayed `replays` times, the outputs scrambled before each replay."""
+    graph replayed `replays` times, the outputs scrambled before each replay.
+    An entry of `outs` may be (tensor, mask): only the masked elements are
+    written by fn and compared."""
+    masks = [o[1] if isinstance(o, tuple) else None for o in outs]
+    outs = [o[0] if isinstance(o, tuple) else o for o in outs]
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -33,7 +37,9 @@ def _replay_check(fn, outs, replays=4):
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        for o, r in zip(outs, ref):
+        for o, r, mk in zip(outs, ref, masks):
+            if mk is not None:
+                o, r = o[mk], r[mk]
             assert torch.equal(o.view(torch.uint8), r.view(torch.uint8)), f"replay {k} differs"
 
 
@@ -103,10 +109,21 @@ def test_graphs_of_every_entry_point():
     o8r = torch.empty((T, H), dtype=torch.uint8, device="cuda")
     s8r = torch.empty((T, H // 128), dtype=torch.float32, device="cuda")
 
+    o8t = torch.empty(T * H, dtype=torch.uint8, device="cuda")
+    s8t = torch.zeros(m.tokblk_scale_count(T, off.size - 1, H), dtype=torch.float32, device="cuda")
+    # the scale entries the call writes: expert e's [H, ceil(n_e/128)] at H (ceil(off_e/128) + e)
+    wmask = torch.zeros(s8t.numel(), dtype=torch.bool)
+    for e in range(off.size - 1):
+        n = int(off[e + 1] - off[e])
+        base = H * (-(-int(off[e]) // 128) + e)
+        wmask[base: base + H * (-(-n // 128))] = True
+    wmask = wmask.cuda()
+
     def f8():
         m.mxfp4_row_to_fp8_col(pk, sb, offd, H, o8, s8)
+        m.mxfp4_row_to_fp8_col_tokblk(pk, sb, offd, H, o8t, s8t)
         m.mxfp4_row_to_fp8_row(pk, sb, H, o8r, s8r)
-    _replay_check(f8, [o8, s8, o8r, s8r])
+    _replay_check(f8, [o8, s8, o8t, (s8t, wmask), o8r, s8r])
 
 
 def test_two_streams_at_once():
@@ -133,6 +150,9 @@ def test_two_streams_at_once():
         with torch.cuda.stream(sb_):
             outs["o8"], outs["s8"] = m.mxfp4_row_to_fp8_col(pk, sb, offd, H, stream=sb_)
             outs["o8r"], outs["s8r"] = m.mxfp4_row_to_fp8_row(pk, sb, H, stream=sb_)
+            nst = m.tokblk_scale_count(T, off.size - 1, H)
+            outs["o8t"], outs["s8t"] = m.mxfp4_row_to_fp8_col_tokblk(
+                pk, sb, offd, H, fp8_scales=torch.zeros(nst, dtype=torch.float32, device="cuda"), stream=sb_)
             outs["q"], _, _ = m.fp4quant_encode_ex(x, 256, "sr", 3, 4, stream=sb_)
         torch.cuda.synchronize()
         return outs
