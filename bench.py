@@ -224,8 +224,8 @@ def fp8col_probe(args, torch, fp4, synth):
 
 def alu_probe(args, torch, fp4, np, synth):
     """The rows judged against the VALU issue rate, each launched `steps`
-    times (PMC runs): NVFP4 SR quantize of 8192x8192 bf16 with a given S_t,
-    and the FP4Quant encoders of the 8192x4096 TP tensor (RTN G=256, SR
+    times (PMC runs): NVFP4 SR quantize of 8192x8192 bf16 and of 4096x7168
+    fp32 with a given S_t, and the FP4Quant encoders of the 8192x4096 TP tensor (RTN G=256, SR
     G=64 and G=256)."""
     g = torch.Generator(device="cuda").manual_seed(11)
     x = (torch.randn((8192, 8192), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
@@ -235,6 +235,13 @@ def alu_probe(args, torch, fp4, np, synth):
     for k in range(args.steps):
         fp4.fp4_quantize(x, "nvfp4", "sr", seed=1, step=k, tscale="given", tensor_scale=ts, packed=p, scales=s)
     del x, p, s
+    xf = torch.randn((4096, 7168), generator=g, device="cuda") * 0.5
+    pf = torch.empty((4096, 3584), dtype=torch.uint8, device="cuda")
+    sf = torch.empty((4096, 448), dtype=torch.uint8, device="cuda")
+    tf = torch.tensor([np.float32(1.0 / 2688)], dtype=torch.float32, device="cuda")
+    for k in range(args.steps):
+        fp4.fp4_quantize(xf, "nvfp4", "sr", seed=1, step=k, tscale="given", tensor_scale=tf, packed=pf, scales=sf)
+    del xf, pf, sf
     tb = synth.tp_tensor()
     xt = torch.from_numpy(tb.view(np.int16)).view(torch.bfloat16).cuda()
     for G in (64, 256):
@@ -413,6 +420,10 @@ def breakdown(args, torch, fp4, np, synth, deferred):
     add("nvfp4_quantize(rtn,given) f32 in", "4096x7168 fp32", 4 * n + n // 2 + n // 16,
         timed(lambda k: fp4.fp4_quantize(xs[k % 4], "nvfp4", "rtn", tscale="given", tensor_scale=ts32,
                                          packed=ps[k % 4], scales=ss16[k % 4]), iters))
+    add("nvfp4_quantize(sr,given) f32 in", "4096x7168 fp32", 4 * n + n // 2 + n // 16,
+        timed(lambda k: fp4.fp4_quantize(xs[k % 4], "nvfp4", "sr", seed=1, step=k, tscale="given",
+                                         tensor_scale=ts32, packed=ps[k % 4], scales=ss16[k % 4]), iters),
+        bound="alu", valu_row="nvfp4 quantize sr, 4096x7168 fp32", elements=n)
     add("mxfp4_dequantize f32 out", "4096x7168 fp32", nb,
         timed(lambda k: fp4.fp4_dequantize(ps[k % 4], ss[k % 4], R, C, "mxfp4", None, torch.float32,
                                            ys[k % 4]), iters))
@@ -845,6 +856,7 @@ def summarize_pmc_kernel(dirs, out, command, prefix, alg, title):
 # Elements per launch of the ALU-bound rows of --profile-mode alu (by kernel
 # name prefix): 8192 x 8192 NVFP4 SR, 8192 x 4096 FP4Quant encoders.
 ALU_ROWS = [("quantize_kernel<true, false, true", "nvfp4 quantize sr, 8192x8192 bf16", 8192 * 8192),
+            ("nv_quantize_f32_kernel<true, false", "nvfp4 quantize sr, 4096x7168 fp32", 4096 * 7168),
             ("fq_encode_rows_kernel<true, 64, true", "fp4quant encode sr G=64, 8192x4096 bf16", 8192 * 4096),
             ("fq_encode_rows_kernel<true, 256, true", "fp4quant encode sr G=256, 8192x4096 bf16", 8192 * 4096),
             ("fq_encode_rows_kernel<true, 256, false", "fp4quant encode rtn G=256, 8192x4096 bf16", 8192 * 4096)]

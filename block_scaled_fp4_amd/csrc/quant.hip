@@ -388,15 +388,19 @@ __global__ __launch_bounds__(kThreads) void nv_rtn_quantize_kernel(
   }
 }
 
-// ------------------------------------------------ NVFP4 RTN from fp32
+// ------------------------------------------------ NVFP4 from fp32
 // Four elements per lane as in mx_quantize_f32_kernel (a 16-element block is
 // 4 lanes: two DPP exchanges for its absmax); scale and codes as in
 // nv_rtn_quantize_kernel, with the IEEE fallback behind the same wave-uniform
-// branch.
-template <int U = 2>
-__global__ __launch_bounds__(kThreads) void nv_rtn_quantize_f32_kernel(
-    const float* __restrict__ x, int64_t n_quad, const float* __restrict__ st_ptr,
-    uint16_t* __restrict__ packed, uint8_t* __restrict__ scales) {
+// branch.  SR: the four draws of a lane are the four words of Philox counter
+// q (elements 4 q .. 4 q + 3), and the quotients are the division-free ones
+// of encode_octet_nv_sr_newton, with IEEE divisions for a lane holding an
+// element or quotient below 2^-100 or a block whose scale left the
+// division-free chain.
+template <bool SR, bool WIDE, int U = 2>
+__global__ __launch_bounds__(kThreads) void nv_quantize_f32_kernel(
+    const float* __restrict__ x, int64_t n_quad, const float* __restrict__ st_ptr, uint64_t seed,
+    uint64_t step, uint16_t* __restrict__ packed, uint8_t* __restrict__ scales) {
   const float st = *st_ptr;
   const bool newton = nv_newton_range(st);
   const float rst = newton ? 1.0f / st : 0.0f;
@@ -420,17 +424,49 @@ __global__ __launch_bounds__(kThreads) void nv_rtn_quantize_f32_kernel(
     bool ok;
     NvScale s = nv_block_scale_newton(am, st, rst, &ok);
     ok = ok && newton;
-    const float y = (s.sdec == 0.0f) ? 0.0f : recip_rn(s.sdec);
-    uint32_t code = cvt_fp4x2_f32<1>(cvt_fp4x2_f32<0>(0u, div_rn(v[0], s.sdec, y), div_rn(v[1], s.sdec, y), 1.0f),
-                                     div_rn(v[2], s.sdec, y), div_rn(v[3], s.sdec, y), 1.0f);
-    if (__ballot(!ok)) {                            // wave-uniform; extreme inputs only
-      if (!ok) {
-        s = nv_block_scale_exact(am, st);
-        code = 0;
+    uint32_t code;
+    if constexpr (SR) {
+      uint32_t c0 = (uint32_t)q, c1 = WIDE ? (uint32_t)((uint64_t)q >> 32) : 0u;
+      uint32_t c2 = (uint32_t)step, c3 = (uint32_t)(step >> 32);
+      philox4x32_10(c0, c1, c2, c3, (uint32_t)seed, (uint32_t)(seed >> 32));
+      const uint32_t u[4] = {c0 >> 8, c1 >> 8, c2 >> 8, c3 >> 8};
+      if (!ok) s = nv_block_scale_exact(am, st);
+      float qv[4];
+      if (ok && s.sdec != 0.0f) {
+        const float y = recip_rn(s.sdec);
+        // |v| >= 2^-100 and |v / sdec| >= 2^-100 (zero excepted), as in encode_octet_nv_sr_newton
+        const uint32_t lim = (__float_as_uint(0x1p-100f * fmaxf(1.0f, s.sdec)) << 1) - 2u;
+        uint32_t small = 0xFFFFFFFFu;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float qv = (s.sdec == 0.0f) ? __builtin_copysignf(0.0f, v[j]) : v[j] / s.sdec;  // IEEE division
-          code |= (e2m1_rtn_mag(fabsf(qv)) | sign_nibble(v[j])) << (4 * j);
+          qv[j] = div_rn(v[j], s.sdec, y);
+          small = min(small, (__float_as_uint(v[j]) << 1) - 2u);
+        }
+        if (small < lim) {                              // rare: IEEE quotients
+#pragma unroll
+          for (int j = 0; j < 4; ++j) qv[j] = v[j] / s.sdec;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          qv[j] = (s.sdec == 0.0f) ? __builtin_copysignf(0.0f, v[j]) : v[j] / s.sdec;  // IEEE division
+      }
+      code = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) code |= (e2m1_sr_mag(fabsf(qv[j]), u[j], false) | sign_nibble(v[j])) << (4 * j);
+    } else {
+      const float y = (s.sdec == 0.0f) ? 0.0f : recip_rn(s.sdec);
+      code = cvt_fp4x2_f32<1>(cvt_fp4x2_f32<0>(0u, div_rn(v[0], s.sdec, y), div_rn(v[1], s.sdec, y), 1.0f),
+                              div_rn(v[2], s.sdec, y), div_rn(v[3], s.sdec, y), 1.0f);
+      if (__ballot(!ok)) {                            // wave-uniform; extreme inputs only
+        if (!ok) {
+          s = nv_block_scale_exact(am, st);
+          code = 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float qv = (s.sdec == 0.0f) ? __builtin_copysignf(0.0f, v[j]) : v[j] / s.sdec;  // IEEE division
+            code |= (e2m1_rtn_mag(fabsf(qv)) | sign_nibble(v[j])) << (4 * j);
+          }
         }
       }
     }
@@ -765,6 +801,20 @@ void launch_quantize_t(bool sr, const void* x, int64_t n_oct, const float* ts, u
     else hipLaunchKernelGGL((mx_quantize_f32_kernel<true, true>), g4, dim3(kThreads), 0, st, xf, n_quad, seed, step, p16, scales);
     return;
   }
+  if constexpr (!MX && !BF16) {
+    if (sr) {
+      // NVFP4 SR from fp32: one lane per four elements, one Philox call each
+      const int64_t n_quad = 2 * n_oct;
+      const dim3 g4((unsigned)blocks_for(n_quad, 2));
+      const float* xf = static_cast<const float*>(x);
+      uint16_t* p16 = reinterpret_cast<uint16_t*>(packed);
+      if (n_quad <= (int64_t(1) << 32))
+        hipLaunchKernelGGL((nv_quantize_f32_kernel<true, false>), g4, dim3(kThreads), 0, st, xf, n_quad, ts, seed, step, p16, scales);
+      else
+        hipLaunchKernelGGL((nv_quantize_f32_kernel<true, true>), g4, dim3(kThreads), 0, st, xf, n_quad, ts, seed, step, p16, scales);
+      return;
+    }
+  }
   const dim3 g((unsigned)blocks_for(n_oct, kOctets<BF16>));
   // SR counters 2 i + 1 below 2^32: their second word is 0 throughout
   if (sr && 2 * n_oct <= (int64_t(1) << 32))
@@ -780,8 +830,8 @@ void launch_quantize_t(bool sr, const void* x, int64_t n_oct, const float* ts, u
                        dim3((unsigned)blocks_for(n_oct, BF16 ? 3 : kOctets<BF16>)), dim3(kThreads), 0, st,
                        x, n_oct, ts, seed, step, packed, scales);
   else if constexpr (!BF16)
-    hipLaunchKernelGGL((nv_rtn_quantize_f32_kernel<2>), dim3((unsigned)blocks_for(2 * n_oct, 2)),
-                       dim3(kThreads), 0, st, static_cast<const float*>(x), 2 * n_oct, ts,
+    hipLaunchKernelGGL((nv_quantize_f32_kernel<false, false>), dim3((unsigned)blocks_for(2 * n_oct, 2)),
+                       dim3(kThreads), 0, st, static_cast<const float*>(x), 2 * n_oct, ts, seed, step,
                        reinterpret_cast<uint16_t*>(packed), scales);
   else
     hipLaunchKernelGGL((nv_rtn_quantize_kernel<BF16>), g, dim3(kThreads), 0, st, x, n_oct, ts,

@@ -321,3 +321,29 @@ def test_nvfp4_sr_bf16_every_pattern_given_scales(step):
                                        step=step)
         np.testing.assert_array_equal(s, rs)
         np.testing.assert_array_equal(p, rp)
+
+
+def test_nvfp4_sr_fp32_quotients_over_the_exponent_range():
+    """NVFP4 SR from fp32 with given tensor scales: the quotient x / s_dec is
+    formed without a division (reciprocal plus one fma correction) where
+    that is the IEEE quotient, and by an IEEE division for elements or
+    quotients below 2^-100 and for blocks whose scale left the division-free
+    chain.  SR reads every bit of the quotient: random fp32 significands over
+    a wide exponent range, including subnormals, against the oracle."""
+    m = need_gpu()
+    rng = np.random.default_rng(77)
+    rows, cols = 256, 1024
+    for st in (1.0, 3.7e-5, 2.0 ** -99, 2.0 ** 99, 2.0 ** -110, 1.5e30):
+        sig = rng.uniform(1.0, 2.0, size=(rows, cols))
+        # per 16-element block a base exponent, per element a spread of 0..40 below it
+        e_blk = rng.integers(-140, 60, size=(rows, cols // 16))
+        e = np.repeat(e_blk, 16, axis=1) - rng.integers(0, 41, size=(rows, cols))
+        x = (np.where(rng.random((rows, cols)) < 0.5, -1.0, 1.0) * sig * np.exp2(e.astype(np.float64))).astype(np.float32)
+        x[rng.random(x.shape) < 0.02] = 0.0
+        assert np.all(np.isfinite(x))
+        ts = dev_f32(np.array([st], np.float32))
+        for step in (0, 5):
+            p, s, _ = run_quant(m, dev_f32(x), "nvfp4", "sr", seed=0xABCDEF, step=step, tscale="given", ts=ts)
+            rp, rs = nvfp4.quantize_packed(x, np.float32(st), "sr", seed=0xABCDEF, step=step)
+            np.testing.assert_array_equal(s, rs, err_msg=f"S_t {st}")
+            np.testing.assert_array_equal(p, rp, err_msg=f"S_t {st}")
