@@ -273,6 +273,21 @@ inline int64_t blocks_for(int64_t items, int per_thread) {
   return (items + per_block - 1) / per_block;
 }
 
+// A dispatch packet holds a grid's size in work-items as a 32-bit count, so
+// a larger 1-D grid would wrap.  launch_1d issues `blocks` workgroups of
+// `threads` in slices of at most 2^31 work-items and passes each slice's
+// first workgroup index as the kernel's last argument (blk0), which the
+// kernel adds to blockIdx.x; below that size it is one launch.
+constexpr int64_t kSliceItems = int64_t(1) << 31;
+template <typename... P, typename... A>
+inline void launch_1d(void (*kernel)(P...), int64_t blocks, int threads, hipStream_t st, A... args) {
+  const int64_t per = kSliceItems / threads;
+  for (int64_t b0 = 0; b0 < blocks; b0 += per) {
+    const int64_t nb = blocks - b0 < per ? blocks - b0 : per;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)nb), dim3((unsigned)threads), 0, st, args..., b0);
+  }
+}
+
 // Grid size for a grid-stride loop over `items` work items of one thread each.
 inline unsigned grid_for(int64_t items, int64_t cap = 256 * 16) {
   int64_t b = (items + kThreads - 1) / kThreads;

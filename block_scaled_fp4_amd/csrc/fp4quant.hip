@@ -165,11 +165,11 @@ template <bool BF16, int EPL, int LPG, bool SR, bool WIDE>
 __global__ __launch_bounds__(kThreads) void fp4quant_encode_kernel(
     const void* __restrict__ x, int64_t n_lane, float inv_g, float c_s2,
     uint32_t* __restrict__ packed, float* __restrict__ s_rms, float* __restrict__ s_abs,
-    uint64_t seed, uint64_t step) {
+    uint64_t seed, uint64_t step, int64_t blk0) {
   constexpr int U = (EPL == 8) ? 2 : 1;
   constexpr int OCT = EPL / 8;
   const int lane = threadIdx.x & 63;
-  const int64_t base = (int64_t)blockIdx.x * (kThreads * U) + threadIdx.x;
+  const int64_t base = ((int64_t)blockIdx.x + blk0) * (kThreads * U) + threadIdx.x;
   float v[U][EPL];
 #pragma unroll
   for (int k = 0; k < U; ++k) {
@@ -216,11 +216,11 @@ __device__ __forceinline__ float group_factor(float s1, float s2, float c_dec, b
 template <bool BF16OUT, int EPL, int LPG>
 __global__ __launch_bounds__(kThreads) void fp4quant_decode_kernel(
     const uint32_t* __restrict__ packed, const float* __restrict__ s_rms,
-    const float* __restrict__ s_abs, int64_t n_lane, float c_dec, void* __restrict__ y) {
+    const float* __restrict__ s_abs, int64_t n_lane, float c_dec, void* __restrict__ y, int64_t blk0) {
   constexpr int U = (EPL == 8) ? 2 : 1;
   constexpr int OCT = EPL / 8;
   const int lane = threadIdx.x & 63;
-  const int64_t base = (int64_t)blockIdx.x * (kThreads * U) + threadIdx.x;
+  const int64_t base = ((int64_t)blockIdx.x + blk0) * (kThreads * U) + threadIdx.x;
   uint32_t w[U][OCT];
   float f[U];
   bool tiny[U];
@@ -446,7 +446,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 template <bool BF16, int G, bool SR, bool WIDE>
 __global__ __launch_bounds__(64 * kRowWaves) void fq_encode_rows_kernel(
     const void* __restrict__ x, int64_t n_oct, uint32_t* __restrict__ packed,
-    float* __restrict__ s_rms, float* __restrict__ s_abs, uint64_t seed, uint64_t step) {
+    float* __restrict__ s_rms, float* __restrict__ s_abs, uint64_t seed, uint64_t step, int64_t blk0) {
   using C = RowCfg<G>;
   constexpr int LPG = C::LPG, S = C::S, D = 64 / LPG, NO = G / 8;
   constexpr int U = kTileOct / (D * NO);             // groups a lane handles in turn
@@ -456,7 +456,7 @@ __global__ __launch_bounds__(64 * kRowWaves) void fq_encode_rows_kernel(
   __shared__ u32x4 tile_codes[kRowWaves][kTileOct / 4];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int gw = lane % D, r = lane / D;
-  const int64_t wave = (int64_t)blockIdx.x * kRowWaves + wv;
+  const int64_t wave = ((int64_t)blockIdx.x + blk0) * kRowWaves + wv;
   const int64_t t0 = wave * kTileOct;                // first octet of the tile
   u32x4* lin = tile_in[wv];
   u32x4* lcodes = tile_codes[wv];
@@ -567,7 +567,7 @@ __global__ __launch_bounds__(64 * kRowWaves) void fq_encode_rows_kernel(
 template <bool BF16OUT, int G>
 __global__ __launch_bounds__(64 * kRowWaves) void fq_decode_rows_kernel(
     const uint32_t* __restrict__ packed, const float* __restrict__ s_rms,
-    const float* __restrict__ s_abs, int64_t n_oct, float c_dec, void* __restrict__ y) {
+    const float* __restrict__ s_abs, int64_t n_oct, float c_dec, void* __restrict__ y, int64_t blk0) {
   using C = RowCfg<G>;
   constexpr int LPG = C::LPG, S = C::S, D = 64 / LPG, NO = G / 8;
   constexpr int U = kTileOct / (D * NO);
@@ -577,7 +577,7 @@ __global__ __launch_bounds__(64 * kRowWaves) void fq_decode_rows_kernel(
   __shared__ u32x4 tile_codes[kRowWaves][kTileOct / 4];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int gw = lane % D, r = lane / D;
-  const int64_t wave = (int64_t)blockIdx.x * kRowWaves + wv;
+  const int64_t wave = ((int64_t)blockIdx.x + blk0) * kRowWaves + wv;
   const int64_t t0 = wave * kTileOct;
   u32x4* lout = tile_out[wv];
   u32x4* lcodes = tile_codes[wv];
@@ -677,9 +677,8 @@ void launch_encode_rows(const void* x, int64_t n, uint32_t* pk, float* s1, float
                         uint64_t seed, uint64_t step, hipStream_t st) {
   const int64_t n_oct = n / 8;
   const int64_t waves = (n_oct + kTileOct - 1) / kTileOct;
-  hipLaunchKernelGGL((fq_encode_rows_kernel<BF16, G, SR, WIDE>),
-                     dim3((unsigned)((waves + kRowWaves - 1) / kRowWaves)), dim3(64 * kRowWaves), 0,
-                     st, x, n_oct, pk, s1, s2, seed, step);
+  launch_1d(fq_encode_rows_kernel<BF16, G, SR, WIDE>, (waves + kRowWaves - 1) / kRowWaves,
+            64 * kRowWaves, st, x, n_oct, pk, s1, s2, seed, step);
 }
 template <bool BF16OUT, int G>
 void launch_decode_rows(const uint32_t* pk, const float* s1, const float* s2, int64_t n, void* y,
@@ -687,9 +686,8 @@ void launch_decode_rows(const uint32_t* pk, const float* s1, const float* s2, in
   const int64_t n_oct = n / 8;
   const int64_t waves = (n_oct + kTileOct - 1) / kTileOct;
   const float c_dec = (float)(0.5 / __builtin_sqrt((double)G));
-  hipLaunchKernelGGL((fq_decode_rows_kernel<BF16OUT, G>),
-                     dim3((unsigned)((waves + kRowWaves - 1) / kRowWaves)), dim3(64 * kRowWaves), 0,
-                     st, pk, s1, s2, n_oct, c_dec, y);
+  launch_1d(fq_decode_rows_kernel<BF16OUT, G>, (waves + kRowWaves - 1) / kRowWaves, 64 * kRowWaves,
+            st, pk, s1, s2, n_oct, c_dec, y);
 }
 
 template <bool BF16, bool SR, bool WIDE>
@@ -700,9 +698,8 @@ void launch_encode_t(int G, const void* x, int64_t n, uint32_t* pk, float* s1, f
 #define FP4MI_ENC(EPL, LPG)                                                                   \
   {                                                                                           \
     int64_t nl = n / EPL;                                                                     \
-    hipLaunchKernelGGL((fp4quant_encode_kernel<BF16, EPL, LPG, SR, WIDE>),                    \
-                       dim3((unsigned)blocks_for(nl, EPL == 8 ? 2 : 1)),                      \
-                       dim3(kThreads), 0, st, x, nl, inv_g, c_s2, pk, s1, s2, seed, step);     \
+    launch_1d(fp4quant_encode_kernel<BF16, EPL, LPG, SR, WIDE>, blocks_for(nl, EPL == 8 ? 2 : 1), \
+              kThreads, st, x, nl, inv_g, c_s2, pk, s1, s2, seed, step);                      \
   }
   switch (G) {
     case 16: launch_encode_rows<BF16, 16, SR, WIDE>(x, n, pk, s1, s2, seed, step, st); break;
@@ -734,9 +731,8 @@ void launch_decode(int G, const uint32_t* pk, const float* s1, const float* s2, 
 #define FP4MI_DEC(EPL, LPG)                                                                   \
   {                                                                                           \
     int64_t nl = n / EPL;                                                                     \
-    hipLaunchKernelGGL((fp4quant_decode_kernel<BF16OUT, EPL, LPG>),                           \
-                       dim3((unsigned)blocks_for(nl, EPL == 8 ? 2 : 1)),                      \
-                       dim3(kThreads), 0, st, pk, s1, s2, nl, c_dec, y);                      \
+    launch_1d(fp4quant_decode_kernel<BF16OUT, EPL, LPG>, blocks_for(nl, EPL == 8 ? 2 : 1),     \
+              kThreads, st, pk, s1, s2, nl, c_dec, y);                                        \
   }
   switch (G) {
     case 16: launch_decode_rows<BF16OUT, 16>(pk, s1, s2, n, y, st); break;
@@ -782,7 +778,6 @@ extern "C" int fp4quant_encode_ex(const void* x, int dtype, int64_t rows, int64_
       overlaps(packed, pb, s_rms, gb) || overlaps(packed, pb, s_abs, gb) ||
       overlaps(s_rms, gb, s_abs, gb))
     return FP4_EOVERLAP;
-  if (blocks_for(n / 8, 1) > 0x7FFFFFFF) return FP4_ESHAPE;
   clear_stale_error();
   hipStream_t st = as_stream(stream);
   uint32_t* pk = reinterpret_cast<uint32_t*>(packed);
@@ -808,7 +803,6 @@ extern "C" int fp4quant_decode(const uint8_t* packed, const float* s_rms, const 
   const int64_t yb = n * es, gb = (n / group) * 4;
   if (overlaps(y, yb, packed, n / 2) || overlaps(y, yb, s_rms, gb) || overlaps(y, yb, s_abs, gb))
     return FP4_EOVERLAP;
-  if (blocks_for(n / 8, 1) > 0x7FFFFFFF) return FP4_ESHAPE;
   clear_stale_error();
   hipStream_t st = as_stream(stream);
   const uint32_t* pk = reinterpret_cast<const uint32_t*>(packed);

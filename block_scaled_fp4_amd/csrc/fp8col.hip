@@ -543,7 +543,7 @@ constexpr int kRowChunks = 2;                         // 16-channel chunks per t
 __global__ __launch_bounds__(kThreads) void fp8row_kernel(const uint8_t* __restrict__ packed,
                                                          const uint32_t* __restrict__ sb4,
                                                          int64_t n_chunk, uint8_t* __restrict__ out,
-                                                         float* __restrict__ sc_out) {
+                                                         float* __restrict__ sc_out, int64_t blk0) {
   __shared__ uint32_t lut[(kMaxShift + 1) * 2];
   if (threadIdx.x < (kMaxShift + 1) * 2) {
     const int d = threadIdx.x >> 1, half = threadIdx.x & 1;
@@ -551,7 +551,7 @@ __global__ __launch_bounds__(kThreads) void fp8row_kernel(const uint8_t* __restr
     for (int k = 0; k < 4; ++k) w |= remap_e2m1_to_e4m3((uint32_t)(4 * half + k), d) << (8 * k);
     lut[threadIdx.x] = w;
   }
-  const int64_t base = (int64_t)blockIdx.x * (kThreads * kRowChunks) + threadIdx.x;
+  const int64_t base = ((int64_t)blockIdx.x + blk0) * (kThreads * kRowChunks) + threadIdx.x;
   u32x2 cw[kRowChunks];
   uint32_t s4[kRowChunks];
 #pragma unroll
@@ -675,10 +675,8 @@ extern "C" int mxfp4_row_to_fp8_row(const uint8_t* packed, const uint8_t* scales
   const int64_t n_sub = n / 32;
   const int64_t n_chunk = 2 * n_sub;
   const int64_t grid = (n_chunk + kThreads * kRowChunks - 1) / (kThreads * kRowChunks);
-  if (grid > 0x7FFFFFFF) return FP4_ESHAPE;
   clear_stale_error();
-  hipLaunchKernelGGL(fp8row_kernel, dim3((unsigned)grid), dim3(kThreads), 0, as_stream(stream),
-                     packed, reinterpret_cast<const uint32_t*>(scales_e8m0), n_chunk, fp8_out,
-                     fp8_scales);
+  launch_1d(fp8row_kernel, grid, kThreads, as_stream(stream), packed,
+            reinterpret_cast<const uint32_t*>(scales_e8m0), n_chunk, fp8_out, fp8_scales);
   return launch_status();
 }

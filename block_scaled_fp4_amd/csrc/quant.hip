@@ -221,11 +221,11 @@ __device__ __forceinline__ uint32_t encode_octet_mx_rtn(const u32x4& raw, const 
 template <bool BF16, bool MX, bool SR, int U = kOctets<BF16>, bool WIDE = true>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(
     const void* __restrict__ x, int64_t n_oct, const float* __restrict__ st_ptr, uint64_t seed,
-    uint64_t step, uint32_t* __restrict__ packed, uint8_t* __restrict__ scales) {
+    uint64_t step, uint32_t* __restrict__ packed, uint8_t* __restrict__ scales, int64_t blk0) {
   const float st = MX ? 1.0f : *st_ptr;
   const bool newton = !MX && nv_newton_range(st);
   const float rst = newton ? 1.0f / st : 0.0f;
-  const int64_t base = (int64_t)blockIdx.x * (kThreads * U) + threadIdx.x;
+  const int64_t base = ((int64_t)blockIdx.x + blk0) * (kThreads * U) + threadIdx.x;
   u32x4 ra[U], rb[U];
 #pragma unroll
   for (int k = 0; k < U; ++k) {
@@ -289,8 +289,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
 template <bool SR, bool WIDE, int U = 2>
 __global__ __launch_bounds__(kThreads) void mx_quantize_f32_kernel(
     const float* __restrict__ x, int64_t n_quad, uint64_t seed, uint64_t step,
-    uint16_t* __restrict__ packed, uint8_t* __restrict__ scales) {
-  const int64_t base = (int64_t)blockIdx.x * (kThreads * U) + threadIdx.x;
+    uint16_t* __restrict__ packed, uint8_t* __restrict__ scales, int64_t blk0) {
+  const int64_t base = ((int64_t)blockIdx.x + blk0) * (kThreads * U) + threadIdx.x;
   u32x4 a[U];
 #pragma unroll
   for (int k = 0; k < U; ++k) {
@@ -343,11 +343,11 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_f32_kernel(
 template <bool BF16, int U = kOctets<BF16>>
 __global__ __launch_bounds__(kThreads) void nv_rtn_quantize_kernel(
     const void* __restrict__ x, int64_t n_oct, const float* __restrict__ st_ptr,
-    uint32_t* __restrict__ packed, uint8_t* __restrict__ scales) {
+    uint32_t* __restrict__ packed, uint8_t* __restrict__ scales, int64_t blk0) {
   const float st = *st_ptr;
   const bool newton = nv_newton_range(st);
   const float rst = newton ? 1.0f / st : 0.0f;
-  const int64_t base = (int64_t)blockIdx.x * (kThreads * U) + threadIdx.x;
+  const int64_t base = ((int64_t)blockIdx.x + blk0) * (kThreads * U) + threadIdx.x;
   u32x4 ra[U], rb[U];
 #pragma unroll
   for (int k = 0; k < U; ++k) {
@@ -400,11 +400,11 @@ __global__ __launch_bounds__(kThreads) void nv_rtn_quantize_kernel(
 template <bool SR, bool WIDE, int U = 2>
 __global__ __launch_bounds__(kThreads) void nv_quantize_f32_kernel(
     const float* __restrict__ x, int64_t n_quad, const float* __restrict__ st_ptr, uint64_t seed,
-    uint64_t step, uint16_t* __restrict__ packed, uint8_t* __restrict__ scales) {
+    uint64_t step, uint16_t* __restrict__ packed, uint8_t* __restrict__ scales, int64_t blk0) {
   const float st = *st_ptr;
   const bool newton = nv_newton_range(st);
   const float rst = newton ? 1.0f / st : 0.0f;
-  const int64_t base = (int64_t)blockIdx.x * (kThreads * U) + threadIdx.x;
+  const int64_t base = ((int64_t)blockIdx.x + blk0) * (kThreads * U) + threadIdx.x;
   u32x4 a[U];
 #pragma unroll
   for (int k = 0; k < U; ++k) {
@@ -494,9 +494,9 @@ __device__ __forceinline__ void mx_dequant_octet_hw(uint32_t w, uint32_t b, void
 template <bool MX, int U = 1>
 __global__ __launch_bounds__(kThreads) void dequantize_kernel(
     const uint32_t* __restrict__ packed, const uint8_t* __restrict__ scales,
-    const float* __restrict__ st_ptr, int64_t n_oct, void* __restrict__ y) {
+    const float* __restrict__ st_ptr, int64_t n_oct, void* __restrict__ y, int64_t blk0) {
   const float st = MX ? 1.0f : *st_ptr;
-  const int64_t base = (int64_t)blockIdx.x * (kThreads * U) + threadIdx.x;
+  const int64_t base = ((int64_t)blockIdx.x + blk0) * (kThreads * U) + threadIdx.x;
   uint32_t w[U], b[U];
 #pragma unroll
   for (int k = 0; k < U; ++k) {
@@ -542,9 +542,9 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(
 template <bool MX, int U = 2>
 __global__ __launch_bounds__(kThreads) void dequantize_f32_kernel(
     const uint16_t* __restrict__ packed, const uint8_t* __restrict__ scales,
-    const float* __restrict__ st_ptr, int64_t n_quad, float* __restrict__ y) {
+    const float* __restrict__ st_ptr, int64_t n_quad, float* __restrict__ y, int64_t blk0) {
   const float st = MX ? 1.0f : *st_ptr;
-  const int64_t base = (int64_t)blockIdx.x * (kThreads * U) + threadIdx.x;
+  const int64_t base = ((int64_t)blockIdx.x + blk0) * (kThreads * U) + threadIdx.x;
   uint32_t w[U], b[U];
 #pragma unroll
   for (int k = 0; k < U; ++k) {
@@ -684,20 +684,22 @@ __global__ void tensor_scale_finalize_kernel(float* ts) {
 }
 
 // ------------------------------------------------- error-feedback qdq
-// KEEP (given S_t): fp32 inputs are read with plain loads.  After the amax
-// pass (computed S_t) they are read with streaming loads, which leave the
-// tail of x and r that the amax pass left in the Infinity Cache in place
+// One lane per octet; launched for bf16 x (fp32 x: ef_qdq_f32_kernel).
+// KEEP (given S_t): fp32 inputs are read with plain loads, so that the line
+// a wave reads in two instructions stays in L2 between them.  After the
+// amax pass (computed S_t) they are read with streaming loads, which leave
+// the tail of x and r that the amax pass left in the Infinity Cache in place
 // until this pass reaches it.
 template <bool BF16IN, bool BF16OUT, bool RES, bool SR, bool CODES, bool KEEP>
 __global__ __launch_bounds__(kThreads) void ef_qdq_kernel(
     const void* x, float* __restrict__ res, void* y, int64_t n_oct,
     const float* __restrict__ st_ptr, uint64_t seed, uint64_t step, uint32_t* __restrict__ packed,
-    uint8_t* __restrict__ scales) {
+    uint8_t* __restrict__ scales, int64_t blk0) {
   constexpr int U = 1;   // one octet per thread measured fastest (loads of x and r in flight)
   const float st = *st_ptr;
   const bool newton = nv_newton_range(st);
   const float rst = newton ? 1.0f / st : 0.0f;
-  const int64_t base = (int64_t)blockIdx.x * (kThreads * U) + threadIdx.x;
+  const int64_t base = ((int64_t)blockIdx.x + blk0) * (kThreads * U) + threadIdx.x;
   float v[U][8];
 #pragma unroll
   for (int k = 0; k < U; ++k) {
@@ -757,6 +759,119 @@ __global__ __launch_bounds__(kThreads) void ef_qdq_kernel(
   }
 }
 
+// Error feedback from fp32 x: four elements per lane as in
+// nv_quantize_f32_kernel (one 16-byte access of x, of r and of an fp32 y per
+// lane, so a wave instruction covers 1 KiB), the codes of that kernel, then
+// the octet kernel's output and residual.  Each lane reads its elements
+// before it writes them, so x may be y and r is updated in place.  One quad
+// per lane with streaming loads measured fastest on 8192 x 8192 (145 us with
+// a given S_t against 152 us with two quads per lane and 167 us with two and
+// plain loads; the octet kernel took 160 us); with a computed S_t as well.
+template <bool BF16OUT, bool RES, bool SR, bool CODES, bool WIDE, int U = 1>
+__global__ __launch_bounds__(kThreads) void ef_qdq_f32_kernel(
+    const float* x, float* __restrict__ res, void* y, int64_t n_quad,
+    const float* __restrict__ st_ptr, uint64_t seed, uint64_t step, uint16_t* __restrict__ packed,
+    uint8_t* __restrict__ scales, int64_t blk0) {
+  const float st = *st_ptr;
+  const bool newton = nv_newton_range(st);
+  const float rst = newton ? 1.0f / st : 0.0f;
+  const int64_t base = ((int64_t)blockIdx.x + blk0) * (kThreads * U) + threadIdx.x;
+  float v[U][4];
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+    const int64_t q = base + (int64_t)k * kThreads;
+    u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+    if (q < n_quad) {
+      a = ld_u32x4(x + 4 * q);
+      if constexpr (RES) b = ld_u32x4(res + 4 * q);
+    }
+    v[k][0] = __uint_as_float(a.x); v[k][1] = __uint_as_float(a.y);
+    v[k][2] = __uint_as_float(a.z); v[k][3] = __uint_as_float(a.w);
+    if constexpr (RES) {
+      v[k][0] = v[k][0] + __uint_as_float(b.x); v[k][1] = v[k][1] + __uint_as_float(b.y);
+      v[k][2] = v[k][2] + __uint_as_float(b.z); v[k][3] = v[k][3] + __uint_as_float(b.w);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+    const int64_t q = base + (int64_t)k * kThreads;
+    const float (&w)[4] = v[k];
+    uint32_t amb = __float_as_uint(fmaxf(fmaxf(fabsf(w[0]), fabsf(w[1])), fmaxf(fabsf(w[2]), fabsf(w[3]))));
+    amb = max(amb, (uint32_t)lane_xor1_i((int)amb));
+    amb = max(amb, (uint32_t)lane_xor2_i((int)amb));
+    const float am = __uint_as_float(amb);
+    bool ok;
+    NvScale s = nv_block_scale_newton(am, st, rst, &ok);
+    ok = ok && newton;
+    uint32_t code;
+    if constexpr (SR) {
+      uint32_t c0 = (uint32_t)q, c1 = WIDE ? (uint32_t)((uint64_t)q >> 32) : 0u;
+      uint32_t c2 = (uint32_t)step, c3 = (uint32_t)(step >> 32);
+      philox4x32_10(c0, c1, c2, c3, (uint32_t)seed, (uint32_t)(seed >> 32));
+      const uint32_t u[4] = {c0 >> 8, c1 >> 8, c2 >> 8, c3 >> 8};
+      if (!ok) s = nv_block_scale_exact(am, st);
+      float qv[4];
+      if (ok && s.sdec != 0.0f) {
+        const float yr = recip_rn(s.sdec);
+        const uint32_t lim = (__float_as_uint(0x1p-100f * fmaxf(1.0f, s.sdec)) << 1) - 2u;
+        uint32_t small = 0xFFFFFFFFu;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          qv[j] = div_rn(w[j], s.sdec, yr);
+          small = min(small, (__float_as_uint(w[j]) << 1) - 2u);
+        }
+        if (small < lim) {                              // rare: IEEE quotients
+#pragma unroll
+          for (int j = 0; j < 4; ++j) qv[j] = w[j] / s.sdec;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          qv[j] = (s.sdec == 0.0f) ? __builtin_copysignf(0.0f, w[j]) : w[j] / s.sdec;  // IEEE division
+      }
+      code = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) code |= (e2m1_sr_mag(fabsf(qv[j]), u[j], false) | sign_nibble(w[j])) << (4 * j);
+    } else {
+      const float yr = (s.sdec == 0.0f) ? 0.0f : recip_rn(s.sdec);
+      code = cvt_fp4x2_f32<1>(cvt_fp4x2_f32<0>(0u, div_rn(w[0], s.sdec, yr), div_rn(w[1], s.sdec, yr), 1.0f),
+                              div_rn(w[2], s.sdec, yr), div_rn(w[3], s.sdec, yr), 1.0f);
+      if (__ballot(!ok)) {                            // wave-uniform; extreme inputs only
+        if (!ok) {
+          s = nv_block_scale_exact(am, st);
+          code = 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float qv = (s.sdec == 0.0f) ? __builtin_copysignf(0.0f, w[j]) : w[j] / s.sdec;  // IEEE division
+            code |= (e2m1_rtn_mag(fabsf(qv)) | sign_nibble(w[j])) << (4 * j);
+          }
+        }
+      }
+    }
+    if (q >= n_quad) continue;
+    const f32x2 d01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 0);
+    const f32x2 d23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 1);
+    float o[4] = {d01.x * s.sdec, d01.y * s.sdec, d23.x * s.sdec, d23.y * s.sdec};
+    if constexpr (BF16OUT) {
+      // round to bf16 once; the residual is taken against the rounded values
+      const uint32_t p0 = pack_bf16x2(o[0], o[1]), p1 = pack_bf16x2(o[2], o[3]);
+      o[0] = __uint_as_float(p0 << 16); o[1] = __uint_as_float(p0 & 0xFFFF0000u);
+      o[2] = __uint_as_float(p1 << 16); o[3] = __uint_as_float(p1 & 0xFFFF0000u);
+      __builtin_nontemporal_store(u32x2{p0, p1}, reinterpret_cast<u32x2*>(static_cast<uint8_t*>(y) + q * 8));
+    } else {
+      st_u32x4(static_cast<float*>(y) + 4 * q,
+               u32x4{__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])});
+    }
+    if constexpr (RES)
+      st_u32x4(res + 4 * q, u32x4{__float_as_uint(w[0] - o[0]), __float_as_uint(w[1] - o[1]),
+                                  __float_as_uint(w[2] - o[2]), __float_as_uint(w[3] - o[3])});
+    if constexpr (CODES) {
+      packed[q] = (uint16_t)code;
+      if ((q & 3) == 0) scales[q >> 2] = (uint8_t)s.code;
+    }
+  }
+}
+
 // ------------------------------------------------------------ launchers
 // S_t into *ts.  With `scratch` (an output buffer of the call that is
 // written only after S_t is known, of scratch_bytes bytes) the workgroups'
@@ -790,70 +905,79 @@ int launch_tensor_scale(const void* x, bool bf16, const float* res, int64_t n_oc
 template <bool BF16, bool MX>
 void launch_quantize_t(bool sr, const void* x, int64_t n_oct, const float* ts, uint64_t seed,
                        uint64_t step, uint32_t* packed, uint8_t* scales, hipStream_t st) {
-  if constexpr (MX && !BF16) {
-    // fp32 input: one lane per four elements
+  if constexpr (!BF16) {
+    // fp32 input: one lane per four elements (MXFP4 both roundings, NVFP4 SR
+    // and RTN), two quads per thread
     const int64_t n_quad = 2 * n_oct;
-    const dim3 g4((unsigned)blocks_for(n_quad, 2));
+    const int64_t g4 = blocks_for(n_quad, 2);
     const float* xf = static_cast<const float*>(x);
     uint16_t* p16 = reinterpret_cast<uint16_t*>(packed);
-    if (!sr) hipLaunchKernelGGL((mx_quantize_f32_kernel<false, false>), g4, dim3(kThreads), 0, st, xf, n_quad, seed, step, p16, scales);
-    else if (n_quad <= (int64_t(1) << 32)) hipLaunchKernelGGL((mx_quantize_f32_kernel<true, false>), g4, dim3(kThreads), 0, st, xf, n_quad, seed, step, p16, scales);
-    else hipLaunchKernelGGL((mx_quantize_f32_kernel<true, true>), g4, dim3(kThreads), 0, st, xf, n_quad, seed, step, p16, scales);
-    return;
-  }
-  if constexpr (!MX && !BF16) {
-    if (sr) {
-      // NVFP4 SR from fp32: one lane per four elements, one Philox call each
-      const int64_t n_quad = 2 * n_oct;
-      const dim3 g4((unsigned)blocks_for(n_quad, 2));
-      const float* xf = static_cast<const float*>(x);
-      uint16_t* p16 = reinterpret_cast<uint16_t*>(packed);
-      if (n_quad <= (int64_t(1) << 32))
-        hipLaunchKernelGGL((nv_quantize_f32_kernel<true, false>), g4, dim3(kThreads), 0, st, xf, n_quad, ts, seed, step, p16, scales);
-      else
-        hipLaunchKernelGGL((nv_quantize_f32_kernel<true, true>), g4, dim3(kThreads), 0, st, xf, n_quad, ts, seed, step, p16, scales);
-      return;
+    const bool wide = n_quad > (int64_t(1) << 32);   // SR counters q need their high word
+    if constexpr (MX) {
+      if (!sr) launch_1d(mx_quantize_f32_kernel<false, false>, g4, kThreads, st, xf, n_quad, seed, step, p16, scales);
+      else if (!wide) launch_1d(mx_quantize_f32_kernel<true, false>, g4, kThreads, st, xf, n_quad, seed, step, p16, scales);
+      else launch_1d(mx_quantize_f32_kernel<true, true>, g4, kThreads, st, xf, n_quad, seed, step, p16, scales);
+    } else {
+      if (!sr) launch_1d(nv_quantize_f32_kernel<false, false>, g4, kThreads, st, xf, n_quad, ts, seed, step, p16, scales);
+      else if (!wide) launch_1d(nv_quantize_f32_kernel<true, false>, g4, kThreads, st, xf, n_quad, ts, seed, step, p16, scales);
+      else launch_1d(nv_quantize_f32_kernel<true, true>, g4, kThreads, st, xf, n_quad, ts, seed, step, p16, scales);
     }
+  } else {
+    const int64_t g = blocks_for(n_oct, kOctets<BF16>);
+    // SR counters 2 i + 1 below 2^32: their second word is 0 throughout
+    if (sr && 2 * n_oct <= (int64_t(1) << 32))
+      launch_1d(quantize_kernel<BF16, MX, true, kOctets<BF16>, false>, g, kThreads, st, x, n_oct, ts,
+                seed, step, packed, scales);
+    else if (sr)
+      launch_1d(quantize_kernel<BF16, MX, true>, g, kThreads, st, x, n_oct, ts, seed, step, packed, scales);
+    else if (MX)
+      // three octets per thread: measured 1% faster than four on 4096 x 7168,
+      // with the input in HBM or in the Infinity Cache
+      launch_1d(quantize_kernel<BF16, true, false, 3>, blocks_for(n_oct, 3), kThreads, st, x, n_oct,
+                ts, seed, step, packed, scales);
+    else
+      launch_1d(nv_rtn_quantize_kernel<BF16>, g, kThreads, st, x, n_oct, ts, packed, scales);
   }
-  const dim3 g((unsigned)blocks_for(n_oct, kOctets<BF16>));
-  // SR counters 2 i + 1 below 2^32: their second word is 0 throughout
-  if (sr && 2 * n_oct <= (int64_t(1) << 32))
-    hipLaunchKernelGGL((quantize_kernel<BF16, MX, true, kOctets<BF16>, false>), g, dim3(kThreads),
-                       0, st, x, n_oct, ts, seed, step, packed, scales);
-  else if (sr)
-    hipLaunchKernelGGL((quantize_kernel<BF16, MX, true>), g, dim3(kThreads), 0, st, x, n_oct,
-                       ts, seed, step, packed, scales);
-  else if (MX)
-    // three octets per thread from bf16 (four from fp32): measured 1% faster
-    // than four on 4096 x 7168, with the input in HBM or in the Infinity Cache
-    hipLaunchKernelGGL((quantize_kernel<BF16, true, false, BF16 ? 3 : kOctets<BF16>>),
-                       dim3((unsigned)blocks_for(n_oct, BF16 ? 3 : kOctets<BF16>)), dim3(kThreads), 0, st,
-                       x, n_oct, ts, seed, step, packed, scales);
-  else if constexpr (!BF16)
-    hipLaunchKernelGGL((nv_quantize_f32_kernel<false, false>), dim3((unsigned)blocks_for(2 * n_oct, 2)),
-                       dim3(kThreads), 0, st, static_cast<const float*>(x), 2 * n_oct, ts, seed, step,
-                       reinterpret_cast<uint16_t*>(packed), scales);
-  else
-    hipLaunchKernelGGL((nv_rtn_quantize_kernel<BF16>), g, dim3(kThreads), 0, st, x, n_oct, ts,
-                       packed, scales);
 }
 
 template <bool BF16IN, bool BF16OUT, bool KEEP>
 void launch_ef_k(bool res, bool sr, bool codes, const void* x, float* r, void* y, int64_t n_oct,
                  const float* ts, uint64_t seed, uint64_t step, uint32_t* packed, uint8_t* scales,
                  hipStream_t st) {
-  const dim3 g((unsigned)blocks_for(n_oct, 1));
-#define FP4MI_EF(RES, SR, CODES)                                                                 \
-  hipLaunchKernelGGL((ef_qdq_kernel<BF16IN, BF16OUT, RES, SR, CODES, KEEP>), g, dim3(kThreads), \
-                     0, st, x, r, y, n_oct, ts, seed, step, packed, scales)
-  if (res) {
-    if (sr) { if (codes) FP4MI_EF(true, true, true); else FP4MI_EF(true, true, false); }
-    else    { if (codes) FP4MI_EF(true, false, true); else FP4MI_EF(true, false, false); }
+  if constexpr (!BF16IN) {
+    // fp32 x: one lane per four elements
+    const int64_t n_quad = 2 * n_oct;
+    const int64_t g4 = blocks_for(n_quad, 1);
+    const float* xf = static_cast<const float*>(x);
+    uint16_t* p16 = reinterpret_cast<uint16_t*>(packed);
+    const bool wide = n_quad > (int64_t(1) << 32);
+#define FP4MI_EF4(RES, SR, CODES, WIDE) \
+  launch_1d(ef_qdq_f32_kernel<BF16OUT, RES, SR, CODES, WIDE>, g4, kThreads, st, xf, r, y, n_quad, ts, seed, step, p16, scales)
+#define FP4MI_EF4_SR(RES, CODES) \
+  do { if (wide) FP4MI_EF4(RES, true, CODES, true); else FP4MI_EF4(RES, true, CODES, false); } while (0)
+    if (res) {
+      if (sr) { if (codes) FP4MI_EF4_SR(true, true); else FP4MI_EF4_SR(true, false); }
+      else    { if (codes) FP4MI_EF4(true, false, true, false); else FP4MI_EF4(true, false, false, false); }
+    } else {
+      if (sr) { if (codes) FP4MI_EF4_SR(false, true); else FP4MI_EF4_SR(false, false); }
+      else    { if (codes) FP4MI_EF4(false, false, true, false); else FP4MI_EF4(false, false, false, false); }
+    }
+#undef FP4MI_EF4_SR
+#undef FP4MI_EF4
   } else {
-    if (sr) { if (codes) FP4MI_EF(false, true, true); else FP4MI_EF(false, true, false); }
-    else    { if (codes) FP4MI_EF(false, false, true); else FP4MI_EF(false, false, false); }
-  }
+    // bf16 x: one lane per octet
+    const int64_t g = blocks_for(n_oct, 1);
+#define FP4MI_EF(RES, SR, CODES) \
+  launch_1d(ef_qdq_kernel<BF16IN, BF16OUT, RES, SR, CODES, KEEP>, g, kThreads, st, x, r, y, n_oct, ts, seed, step, packed, scales)
+    if (res) {
+      if (sr) { if (codes) FP4MI_EF(true, true, true); else FP4MI_EF(true, true, false); }
+      else    { if (codes) FP4MI_EF(true, false, true); else FP4MI_EF(true, false, false); }
+    } else {
+      if (sr) { if (codes) FP4MI_EF(false, true, true); else FP4MI_EF(false, true, false); }
+      else    { if (codes) FP4MI_EF(false, false, true); else FP4MI_EF(false, false, false); }
+    }
 #undef FP4MI_EF
+  }
 }
 
 template <bool BF16IN, bool BF16OUT>
@@ -864,8 +988,6 @@ void launch_ef_t(bool res, bool sr, bool codes, bool given, const void* x, float
   else launch_ef_k<BF16IN, BF16OUT, false>(res, sr, codes, x, r, y, n_oct, ts, seed, step, packed, scales, st);
 }
 
-// Exact grids must fit the x dimension of a launch.
-inline bool grid_fits(int64_t n_oct) { return blocks_for(n_oct, 1) <= 0x7FFFFFFF; }
 
 }  // namespace
 }  // namespace fp4mi
@@ -899,7 +1021,6 @@ extern "C" int fp4_quantize(const void* x, int dtype, int64_t rows, int64_t cols
   hipStream_t st = as_stream(stream);
   const bool bf16 = dtype == FP4_DTYPE_BF16, sr = rounding == FP4_ROUND_SR;
   const int64_t n_oct = n / 8;
-  if (!grid_fits(n_oct)) return FP4_ESHAPE;
   if (!mx && tscale_mode == FP4_TSCALE_COMPUTE) {
     // the packed codes are written only after S_t: their buffer holds the
     // amax pass's partial maxima meanwhile
@@ -939,10 +1060,8 @@ extern "C" int fp4_dequantize(const uint8_t* packed, const uint8_t* scales,
   clear_stale_error();
   hipStream_t st = as_stream(stream);
   const int64_t n_oct = n / 8;
-  if (!grid_fits(n_oct)) return FP4_ESHAPE;
   // two octets per thread: two code loads in flight per lane
   constexpr int U = 2;
-  const dim3 g((unsigned)blocks_for(n_oct, U));
   const uint32_t* pk = reinterpret_cast<const uint32_t*>(packed);
   if (out_dtype == FP4_DTYPE_BF16) {
     // MXFP4 to bf16: eight octets per thread, all eight code loads issued
@@ -951,15 +1070,15 @@ extern "C" int fp4_dequantize(const uint8_t* packed, const uint8_t* scales,
     // with two octets per thread; with codes still in the Infinity Cache two
     // octets are faster (11.6 us against 12.5 us).
     constexpr int UM = 8;
-    if (mx) hipLaunchKernelGGL((dequantize_kernel<true, UM>), dim3((unsigned)blocks_for(n_oct, UM)), dim3(kThreads), 0, st, pk, scales, tensor_scale, n_oct, y);
-    else    hipLaunchKernelGGL((dequantize_kernel<false, U>), dim3(g), dim3(kThreads), 0, st, pk, scales, tensor_scale, n_oct, y);
+    if (mx) launch_1d(dequantize_kernel<true, UM>, blocks_for(n_oct, UM), kThreads, st, pk, scales, tensor_scale, n_oct, y);
+    else    launch_1d(dequantize_kernel<false, U>, blocks_for(n_oct, U), kThreads, st, pk, scales, tensor_scale, n_oct, y);
   } else {
     const int64_t n_quad = 2 * n_oct;
-    const dim3 g4((unsigned)blocks_for(n_quad, U));
+    const int64_t g4 = blocks_for(n_quad, U);
     const uint16_t* p16 = reinterpret_cast<const uint16_t*>(packed);
     float* yf = static_cast<float*>(y);
-    if (mx) hipLaunchKernelGGL((dequantize_f32_kernel<true, U>), g4, dim3(kThreads), 0, st, p16, scales, tensor_scale, n_quad, yf);
-    else    hipLaunchKernelGGL((dequantize_f32_kernel<false, U>), g4, dim3(kThreads), 0, st, p16, scales, tensor_scale, n_quad, yf);
+    if (mx) launch_1d(dequantize_f32_kernel<true, U>, g4, kThreads, st, p16, scales, tensor_scale, n_quad, yf);
+    else    launch_1d(dequantize_f32_kernel<false, U>, g4, kThreads, st, p16, scales, tensor_scale, n_quad, yf);
   }
   return launch_status();
 }
@@ -1000,7 +1119,6 @@ extern "C" int fp4_errfeedback_qdq(const void* x, int dtype, int64_t rows, int64
   const bool bf16 = dtype == FP4_DTYPE_BF16, obf16 = out_dtype == FP4_DTYPE_BF16;
   const bool sr = rounding == FP4_ROUND_SR, codes = packed != nullptr;
   const int64_t n_oct = n / 8;
-  if (!grid_fits(n_oct)) return FP4_ESHAPE;
   if (tscale_mode == FP4_TSCALE_COMPUTE) {
     // the amax partials go to an output the encode pass only writes: the
     // packed codes if requested, else y unless y is x

@@ -248,3 +248,67 @@ def test_mxfp4_sr_from_fp32_past_2_34_elements():
     rp, rs = mxfp4.quantize_packed(xs, "sr", seed=seed, step=step, row_ids=ids)
     np.testing.assert_array_equal(host(s[t]), rs)
     np.testing.assert_array_equal(host(p[t]), rp)
+
+
+def test_nvfp4_sr_and_errfeedback_from_fp32_past_2_34_elements():
+    """NVFP4 stochastic rounding from fp32, then error feedback from fp32 x
+    with an fp32 residual, over 2^34 + 2^21 elements (x and r 64 GiB each):
+    the four-element lanes of the last rows draw from Philox counters with a
+    non-zero high word.  Codes and scales of the quantize, W and the new
+    residual of the error-feedback step, on sampled rows including the last,
+    bit for bit."""
+    m = need_gpu()
+    R, C = (1 << 19) + 64, 1 << 15
+    _need_memory(R * C * (4 + 4 + 2))
+    x = torch.empty((R, C), dtype=torch.float32, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(17)
+    x.normal_(0.0, 1.5, generator=g)
+    st = np.float32(6.0 / 2688)
+    ts = torch.tensor([st], dtype=torch.float32, device="cuda")
+    seed, step = 0x00C0FFEE12345678, (1 << 34) + 3
+    ids = [0, R // 3, R - 65, R - 64, R - 1]            # the last 64 rows lie past 2^34
+    t = torch.tensor(ids, device="cuda")
+    xs = host(x[t])
+    p, s, _ = m.fp4_quantize(x, "nvfp4", "sr", seed=seed, step=step, tscale="given", tensor_scale=ts)
+    torch.cuda.synchronize()
+    rp, rs = nvfp4.quantize_packed(xs, st, "sr", seed=seed, step=step, row_ids=ids)
+    np.testing.assert_array_equal(host(s[t]), rs)
+    np.testing.assert_array_equal(host(p[t]), rp)
+    del p, s
+    torch.cuda.empty_cache()
+    r = torch.empty((R, C), dtype=torch.float32, device="cuda")
+    r.normal_(0.0, 0.05, generator=g)
+    rs_in = host(r[t])
+    w = torch.empty((R, C), dtype=torch.bfloat16, device="cuda")
+    m.fp4_errfeedback_qdq(x, r, w, None, "sr", seed, step + 1, "given", ts)
+    torch.cuda.synchronize()
+    oy, orr, _, _, _ = nvfp4.errfeedback_qdq(xs, rs_in, st, "sr", seed=seed, step=step + 1, row_ids=ids)
+    np.testing.assert_array_equal(host_bf16(w[t]), oy)
+    np.testing.assert_array_equal(host(r[t]).view(np.uint32), orr.view(np.uint32))
+
+
+def test_errfeedback_bf16_in_place_past_2_34_elements():
+    """In-place error feedback of a bf16 weight of 2^34 + 2^21 elements with
+    an fp32 residual (one lane per octet: more than 2^31 work-items, so the
+    grid is issued in slices), SR with Philox counters past 2^32: W and the
+    new residual of sampled rows, including the last, bit for bit."""
+    m = need_gpu()
+    R, C = (1 << 19) + 64, 1 << 15
+    _need_memory(R * C * (2 + 4))
+    w = _fill(R, C, 18)
+    r = torch.empty((R, C), dtype=torch.float32, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(19)
+    r.normal_(0.0, 0.05, generator=g)
+    st = np.float32(4.5 / 2688)
+    ts = torch.tensor([st], dtype=torch.float32, device="cuda")
+    seed, step = 0x1357924680ABCDEF, (1 << 36) + 1
+    ids = [0, R // 3, R - 65, R - 64, R - 1]            # the last 64 rows lie past 2^34
+    t = torch.tensor(ids, device="cuda")
+    ws, rs_in = _rows(w, ids), host(r[t])
+    m.fp4_errfeedback_qdq(w, r, w, None, "sr", seed, step, "given", ts)
+    torch.cuda.synchronize()
+    oy, orr, _, _, _ = nvfp4.errfeedback_qdq(ws, rs_in, st, "sr", seed=seed, step=step, row_ids=ids)
+    np.testing.assert_array_equal(host_bf16(w[t]), oy)
+    np.testing.assert_array_equal(host(r[t]).view(np.uint32), orr.view(np.uint32))
