@@ -15,6 +15,9 @@
  * reports a launch failure; faults inside a kernel surface through HIP at
  * the next synchronisation.  A call on an empty tensor (rows*cols == 0, or
  * total_tokens == 0) is a no-op that returns FP4_OK and writes nothing.
+ * Element counts rows*cols of 2^46 or more are FP4_ESHAPE; below that, any
+ * size that fits in device memory is accepted (grids of more than 2^31
+ * work-items are issued in slices).
  *
  * Layout conventions: tensors are dense row-major [rows, cols]; blocks and
  * groups are contiguous runs along cols.  An E2M1 code is 4 bits: bit 3 is
