@@ -53,10 +53,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // Load 8 consecutive elements (element index 8*i .. 8*i+7) as fp32.
-// KEEP: the two 16-byte halves of an fp32 octet are read with plain (cached)
-// loads instead of streaming ones, so that the line a wave reads in two
-// instructions stays in L2 between them.
-template <bool BF16, bool KEEP = false>
+template <bool BF16>
 __device__ __forceinline__ void load8(const void* base, int64_t i, float (&v)[8]) {
   if constexpr (BF16) {
     u32x4 w = ld_u32x4(static_cast<const uint8_t*>(base) + i * 16);
@@ -64,7 +61,7 @@ __device__ __forceinline__ void load8(const void* base, int64_t i, float (&v)[8]
     v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z); v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
   } else {
     const uint8_t* p = static_cast<const uint8_t*>(base) + i * 32;
-    u32x4 a = KEEP ? ld_u32x4_keep(p) : ld_u32x4(p), b = KEEP ? ld_u32x4_keep(p + 16) : ld_u32x4(p + 16);
+    u32x4 a = ld_u32x4(p), b = ld_u32x4(p + 16);
     v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y);
     v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
     v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y);

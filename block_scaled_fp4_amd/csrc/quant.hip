@@ -707,92 +707,20 @@ __global__ void tensor_scale_finalize_kernel(float* ts) {
 }
 
 // ------------------------------------------------- error-feedback qdq
-// One lane per octet; launched for bf16 x (fp32 x: ef_qdq_f32_kernel).
-// KEEP (given S_t): fp32 inputs are read with plain loads, so that the line
-// a wave reads in two instructions stays in L2 between them.  After the
-// amax pass (computed S_t) they are read with streaming loads, which leave
-// the tail of x and r that the amax pass left in the Infinity Cache in place
-// until this pass reaches it.
-template <bool BF16IN, bool BF16OUT, bool RES, bool SR, bool CODES, bool KEEP>
+// v = x + r, its NVFP4 codes under S_t, the dequantized W = codes * s_dec
+// (rounded once to bf16 for bf16 output, the residual taken against the
+// rounded value) and the new residual v - W.  Four elements per lane as in
+// nv_quantize_f32_kernel (a 16-element block is 4 lanes): one 16-byte access
+// of r and of an fp32 x or y per lane, 8 bytes of a bf16 one, so a wave
+// instruction covers whole lines; the codes are those of that kernel.  Each
+// lane reads its elements before it writes them, so x may be y and r is
+// updated in place.  On 8192 x 8192 with a given S_t this took 145 us from
+// fp32 x (160 us with an octet per lane, 152 us with two quads per lane,
+// 167 us with two and plain loads) and 125 us from bf16 x in place (135 us
+// with an octet per lane).
+template <bool BF16IN, bool BF16OUT, bool RES, bool SR, bool CODES, bool WIDE, int U = 1>
 __global__ __launch_bounds__(kThreads) void ef_qdq_kernel(
-    const void* x, float* __restrict__ res, void* y, int64_t n_oct,
-    const float* __restrict__ st_ptr, uint64_t seed, uint64_t step, uint32_t* __restrict__ packed,
-    uint8_t* __restrict__ scales, int64_t blk0) {
-  constexpr int U = 1;   // one octet per thread measured fastest (loads of x and r in flight)
-  const float st = *st_ptr;
-  const bool newton = nv_newton_range(st);
-  const float rst = newton ? 1.0f / st : 0.0f;
-  const int64_t base = ((int64_t)blockIdx.x + blk0) * (kThreads * U) + threadIdx.x;
-  float v[U][8];
-#pragma unroll
-  for (int k = 0; k < U; ++k) {
-    const int64_t i = base + (int64_t)k * kThreads;
-    const bool ok = i < n_oct;
-    if (ok) load8<BF16IN, KEEP>(x, i, v[k]);
-    else for (int j = 0; j < 8; ++j) v[k][j] = 0.0f;
-    if constexpr (RES) {
-      float rr[8];
-      if (ok) load8<false, KEEP>(res, i, rr);
-      else for (int j = 0; j < 8; ++j) rr[j] = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[k][j] = v[k][j] + rr[j];
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < U; ++k) {
-    const int64_t i = base + (int64_t)k * kThreads;
-    float am = absmax8(v[k]);
-    am = fmaxf(am, lane_xor1(am));
-    bool ok;
-    NvScale s = nv_block_scale_newton(am, st, rst, &ok);
-    ok = ok && newton;
-    if (!ok) s = nv_block_scale_exact(am, st);
-    uint32_t word;
-    if constexpr (SR) word = encode_octet_sw<false, true>(v[k], s.sdec, 0, i, seed, step);
-    else word = ok ? encode_octet_nv_rtn(v[k], s.sdec)
-                   : encode_octet_sw<false, false>(v[k], s.sdec, 0, i, 0, 0);
-    if (i >= n_oct) continue;
-    float o[8];
-    e2m1x8_to_f32(word, 1.0f, o);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) o[j] = o[j] * s.sdec;
-    if constexpr (BF16OUT) {
-      // round to bf16 once; the residual is taken against the rounded values
-      uint32_t pr[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        pr[j] = pack_bf16x2(o[2 * j], o[2 * j + 1]);
-        o[2 * j] = __uint_as_float(pr[j] << 16);
-        o[2 * j + 1] = __uint_as_float(pr[j] & 0xFFFF0000u);
-      }
-      st_u32x4(static_cast<uint8_t*>(y) + i * 16, u32x4{pr[0], pr[1], pr[2], pr[3]});
-    } else {
-      store8<false>(y, i, o);
-    }
-    if constexpr (RES) {
-      float rn[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) rn[j] = v[k][j] - o[j];
-      store8<false>(res, i, rn);
-    }
-    if constexpr (CODES) {
-      st_u32(packed + i, word);
-      if ((i & 1) == 0) scales[i >> 1] = (uint8_t)s.code;
-    }
-  }
-}
-
-// Error feedback from fp32 x: four elements per lane as in
-// nv_quantize_f32_kernel (one 16-byte access of x, of r and of an fp32 y per
-// lane, so a wave instruction covers 1 KiB), the codes of that kernel, then
-// the octet kernel's output and residual.  Each lane reads its elements
-// before it writes them, so x may be y and r is updated in place.  One quad
-// per lane with streaming loads measured fastest on 8192 x 8192 (145 us with
-// a given S_t against 152 us with two quads per lane and 167 us with two and
-// plain loads; the octet kernel took 160 us); with a computed S_t as well.
-template <bool BF16OUT, bool RES, bool SR, bool CODES, bool WIDE, int U = 1>
-__global__ __launch_bounds__(kThreads) void ef_qdq_f32_kernel(
-    const float* x, float* __restrict__ res, void* y, int64_t n_quad,
+    const void* x, float* __restrict__ res, void* y, int64_t n_quad,
     const float* __restrict__ st_ptr, uint64_t seed, uint64_t step, uint16_t* __restrict__ packed,
     uint8_t* __restrict__ scales, int64_t blk0) {
   const float st = *st_ptr;
@@ -805,7 +733,13 @@ __global__ __launch_bounds__(kThreads) void ef_qdq_f32_kernel(
     const int64_t q = base + (int64_t)k * kThreads;
     u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
     if (q < n_quad) {
-      a = ld_u32x4(x + 4 * q);
+      if constexpr (BF16IN) {
+        const u32x2 h = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x2*>(static_cast<const uint8_t*>(x) + 8 * q));
+        a = u32x4{h.x << 16, h.x & 0xFFFF0000u, h.y << 16, h.y & 0xFFFF0000u};
+      } else {
+        a = ld_u32x4(static_cast<const float*>(x) + 4 * q);
+      }
       if constexpr (RES) b = ld_u32x4(res + 4 * q);
     }
     v[k][0] = __uint_as_float(a.x); v[k][1] = __uint_as_float(a.y);
@@ -963,52 +897,28 @@ void launch_quantize_t(bool sr, const void* x, int64_t n_oct, const float* ts, u
   }
 }
 
-template <bool BF16IN, bool BF16OUT, bool KEEP>
-void launch_ef_k(bool res, bool sr, bool codes, const void* x, float* r, void* y, int64_t n_oct,
+template <bool BF16IN, bool BF16OUT>
+void launch_ef_t(bool res, bool sr, bool codes, const void* x, float* r, void* y, int64_t n_oct,
                  const float* ts, uint64_t seed, uint64_t step, uint32_t* packed, uint8_t* scales,
                  hipStream_t st) {
-  if constexpr (!BF16IN) {
-    // fp32 x: one lane per four elements
-    const int64_t n_quad = 2 * n_oct;
-    const int64_t g4 = blocks_for(n_quad, 1);
-    const float* xf = static_cast<const float*>(x);
-    uint16_t* p16 = reinterpret_cast<uint16_t*>(packed);
-    const bool wide = n_quad > (int64_t(1) << 32);
-#define FP4MI_EF4(RES, SR, CODES, WIDE) \
-  launch_1d(ef_qdq_f32_kernel<BF16OUT, RES, SR, CODES, WIDE>, g4, kThreads, st, xf, r, y, n_quad, ts, seed, step, p16, scales)
-#define FP4MI_EF4_SR(RES, CODES) \
-  do { if (wide) FP4MI_EF4(RES, true, CODES, true); else FP4MI_EF4(RES, true, CODES, false); } while (0)
-    if (res) {
-      if (sr) { if (codes) FP4MI_EF4_SR(true, true); else FP4MI_EF4_SR(true, false); }
-      else    { if (codes) FP4MI_EF4(true, false, true, false); else FP4MI_EF4(true, false, false, false); }
-    } else {
-      if (sr) { if (codes) FP4MI_EF4_SR(false, true); else FP4MI_EF4_SR(false, false); }
-      else    { if (codes) FP4MI_EF4(false, false, true, false); else FP4MI_EF4(false, false, false, false); }
-    }
-#undef FP4MI_EF4_SR
-#undef FP4MI_EF4
+  const int64_t n_quad = 2 * n_oct;
+  const int64_t g4 = blocks_for(n_quad, 1);
+  uint16_t* p16 = reinterpret_cast<uint16_t*>(packed);
+  const bool wide = n_quad > (int64_t(1) << 32);     // SR counters q need their high word
+#define FP4MI_EF(RES, SR, CODES, WIDE)                                                           \
+  launch_1d(ef_qdq_kernel<BF16IN, BF16OUT, RES, SR, CODES, WIDE>, g4, kThreads, st, x, r, y, n_quad, \
+            ts, seed, step, p16, scales)
+#define FP4MI_EF_SR(RES, CODES) \
+  do { if (wide) FP4MI_EF(RES, true, CODES, true); else FP4MI_EF(RES, true, CODES, false); } while (0)
+  if (res) {
+    if (sr) { if (codes) FP4MI_EF_SR(true, true); else FP4MI_EF_SR(true, false); }
+    else    { if (codes) FP4MI_EF(true, false, true, false); else FP4MI_EF(true, false, false, false); }
   } else {
-    // bf16 x: one lane per octet
-    const int64_t g = blocks_for(n_oct, 1);
-#define FP4MI_EF(RES, SR, CODES) \
-  launch_1d(ef_qdq_kernel<BF16IN, BF16OUT, RES, SR, CODES, KEEP>, g, kThreads, st, x, r, y, n_oct, ts, seed, step, packed, scales)
-    if (res) {
-      if (sr) { if (codes) FP4MI_EF(true, true, true); else FP4MI_EF(true, true, false); }
-      else    { if (codes) FP4MI_EF(true, false, true); else FP4MI_EF(true, false, false); }
-    } else {
-      if (sr) { if (codes) FP4MI_EF(false, true, true); else FP4MI_EF(false, true, false); }
-      else    { if (codes) FP4MI_EF(false, false, true); else FP4MI_EF(false, false, false); }
-    }
-#undef FP4MI_EF
+    if (sr) { if (codes) FP4MI_EF_SR(false, true); else FP4MI_EF_SR(false, false); }
+    else    { if (codes) FP4MI_EF(false, false, true, false); else FP4MI_EF(false, false, false, false); }
   }
-}
-
-template <bool BF16IN, bool BF16OUT>
-void launch_ef_t(bool res, bool sr, bool codes, bool given, const void* x, float* r, void* y,
-                 int64_t n_oct, const float* ts, uint64_t seed, uint64_t step, uint32_t* packed,
-                 uint8_t* scales, hipStream_t st) {
-  if (given) launch_ef_k<BF16IN, BF16OUT, true>(res, sr, codes, x, r, y, n_oct, ts, seed, step, packed, scales, st);
-  else launch_ef_k<BF16IN, BF16OUT, false>(res, sr, codes, x, r, y, n_oct, ts, seed, step, packed, scales, st);
+#undef FP4MI_EF_SR
+#undef FP4MI_EF
 }
 
 
@@ -1152,13 +1062,12 @@ extern "C" int fp4_errfeedback_qdq(const void* x, int dtype, int64_t rows, int64
   }
   uint32_t* pk = reinterpret_cast<uint32_t*>(packed);
   const bool res = residual != nullptr;
-  const bool given = tscale_mode == FP4_TSCALE_GIVEN;
   if (bf16) {
-    if (obf16) launch_ef_t<true, true>(res, sr, codes, given, x, residual, y, n_oct, tensor_scale, seed, step, pk, scales, st);
-    else       launch_ef_t<true, false>(res, sr, codes, given, x, residual, y, n_oct, tensor_scale, seed, step, pk, scales, st);
+    if (obf16) launch_ef_t<true, true>(res, sr, codes, x, residual, y, n_oct, tensor_scale, seed, step, pk, scales, st);
+    else       launch_ef_t<true, false>(res, sr, codes, x, residual, y, n_oct, tensor_scale, seed, step, pk, scales, st);
   } else {
-    if (obf16) launch_ef_t<false, true>(res, sr, codes, given, x, residual, y, n_oct, tensor_scale, seed, step, pk, scales, st);
-    else       launch_ef_t<false, false>(res, sr, codes, given, x, residual, y, n_oct, tensor_scale, seed, step, pk, scales, st);
+    if (obf16) launch_ef_t<false, true>(res, sr, codes, x, residual, y, n_oct, tensor_scale, seed, step, pk, scales, st);
+    else       launch_ef_t<false, false>(res, sr, codes, x, residual, y, n_oct, tensor_scale, seed, step, pk, scales, st);
   }
   return launch_status();
 }
