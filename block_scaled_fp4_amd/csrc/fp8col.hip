@@ -111,6 +111,7 @@ __device__ __forceinline__ int clampT(int64_t v, int T) {
 struct ColPlan {
   int bp;              // block pair of the item
   int off1, n1, u1;    // loader: expert of the lane's 4 positions, first local index
+  int e1;              // loader: that expert's index
   int off2, n2, u2;    // storer: expert of the lane's chunk, its first local index
 };
 
@@ -183,6 +184,50 @@ __device__ int find_expert_t(const int64_t* off, const int* offs, int E, int T, 
   return lo;
 }
 
+// Dense 128-position layout of the token-block kernel: expert e starts at
+// position 128 pst[e], pst being the exclusive prefix sum of ceil(n_e / 128)
+// (in LDS).  Experts with no tokens take no slot, so several can share a
+// start; the search returns the last expert starting at or before P.
+__device__ int find_expert_dense(const int* pst, int E, int P, int lane) {
+  int lo = 0, hi = E;
+  while (hi - lo > 1) {
+    const int step = (hi - lo + 63) / 64;
+    const int e = lo + lane * step;
+    const bool le = e < hi && 128 * pst[e] <= P;
+    const uint64_t m = __ballot(le);
+    const int last = m ? 63 - __builtin_clzll(m) : 0;
+    lo += last * step;
+    hi = min(lo + step, hi);
+  }
+  return lo;
+}
+
+// Plan of item (tile, bp) in the dense layout: every 128-position slot lies
+// in one expert (or past the last one), so the four slots' experts are found
+// first (lane k holds slot k's) and each lane takes the one of its slot.
+__device__ __forceinline__ ColPlan plan_item_dense(const int* offs, const int* pst, int E, int tile,
+                                                   int bp, int lane, int g, int q2) {
+  const int P0 = tile * kCTile;
+  int se = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int ek = find_expert_dense(pst, E, P0 + 128 * k, lane);
+    se = (lane == k) ? ek : se;
+  }
+  const int s_off = offs[se], s_n = max(offs[se + 1] - s_off, 0), s_poff = 128 * pst[se];
+  const int k1 = g >> 5, k2 = q2 >> 3;          // slots of the loader positions and of the chunk
+  ColPlan p;
+  p.bp = bp;
+  p.off1 = __shfl(s_off, k1);
+  p.n1 = __shfl(s_n, k1);
+  p.u1 = P0 + 4 * g - __shfl(s_poff, k1);
+  p.e1 = __shfl(se, k1);
+  p.off2 = __shfl(s_off, k2);
+  p.n2 = __shfl(s_n, k2);
+  p.u2 = P0 + 16 * q2 - __shfl(s_poff, k2);
+  return p;
+}
+
 // Plan of item (tile, bp): candidate experts e_base + lane (e_base starts at
 // or before the tile), then per chunk the last candidate starting at or
 // before it.
@@ -214,6 +259,7 @@ __device__ __forceinline__ ColPlan plan_item(const int64_t* off, const int* offs
   p.off1 = __shfl(c_off, i1);
   p.n1 = __shfl(c_n, i1);
   p.u1 = P0 + 16 * q1 - __shfl(c_poff, i1) + 4 * (g & 3);
+  p.e1 = eb + i1;
   p.off2 = __shfl(c_off, i2);
   p.n2 = __shfl(c_n, i2);
   p.u2 = P0 + 16 * q2 - __shfl(c_poff, i2);
@@ -367,10 +413,16 @@ int launch_fp8col_tiles(const uint8_t* packed, const uint8_t* sb, const int64_t*
 // transpose, block j of channel h is tokens 128 j .. 128 j + 127 of the
 // expert, and its target scale is the largest UE8M0 byte of those tokens for
 // the channel's 32-channel group (a partial last block uses the tokens it
-// has).  The tiles of fp8col_tiles_kernel are reused with experts padded to
-// 128 positions (expert e starts at position 128 (ceil(off_e / 128) + e)), so
-// every 128-position slot of a 512-position tile is one token block of one
-// expert or padding.  Per item:
+// has).  The tiles of fp8col_tiles_kernel are reused with every expert
+// starting on a multiple of 128 positions, so every 128-position slot of a
+// 512-position tile is one token block of one expert or padding.  With
+// E + 1 <= kOffLds each workgroup first builds the dense layout in LDS
+// (expert e at slot pst[e], the exclusive prefix sum of ceil(n_e / 128), and
+// the item count from its total); otherwise, or when malformed offsets make
+// that layout longer, expert e starts at slot ceil(off_e / 128) + e, a closed
+// form that needs no prefix sum but pads every expert by up to a slot more
+// (on 65,536 tokens over 256 Zipf(1.1) experts, 768 slots against 652).
+// Per item:
 //   1. each loader lane takes the largest sub-block byte of its 4 tokens; a
 //      wave reduces its 8 lanes of each sub-block with shuffles and LDS
 //      max-atomics combine the 4 waves of a slot: S_tgt[slot][sub-block];
@@ -379,7 +431,7 @@ int launch_fp8col_tiles(const uint8_t* packed, const uint8_t* sb, const int64_t*
 //      writes the fp32 scale 2^(S_tgt - 127) of its channel and block;
 //   3. after a second barrier the rows are stored as before.
 // Expert e's scales form an [H, ceil(n_e / 128)] matrix at element
-// H (ceil(off_e / 128) + e): a closed form of the offsets, so no prefix sum.
+// H (ceil(off_e / 128) + e) in either layout: a closed form of the offsets.
 template <bool LDS_TABLE>
 __global__ __launch_bounds__(kCThreads) void fp8col_tokblk_kernel(
     const uint8_t* __restrict__ packed, const uint8_t* __restrict__ sb,
@@ -390,14 +442,17 @@ __global__ __launch_bounds__(kCThreads) void fp8col_tokblk_kernel(
   __shared__ int offs[LDS_TABLE ? kOffLds : 1];
   __shared__ uint32_t tmax[4][8];       // S_tgt per (128-position slot, sub-block of the pair)
   __shared__ int slot_u[4], slot_n[4];  // local index of the slot's first position, expert size
+  __shared__ int slot_b[4];             // the expert's first scale block: ceil(off / 128) + e
+  __shared__ int pst[LDS_TABLE ? kOffLds : 1];   // dense layout: first slot of each expert
+  __shared__ int wsum[kCThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int s8 = lane & 7, g = 8 * wave + (lane >> 3), q1 = g >> 2, q2 = lane & 31;
   const int slot = wave >> 2;           // the loader lane's slot: positions 128 slot ..
   const int64_t HB = H / 128;
   const int xcd = (int)(blockIdx.x % kXcds), sl = (int)(blockIdx.x / kXcds);
-  const int64_t i0 = xcd * ipx, i1 = min(i0 + ipx, nitems);
+  int64_t i0 = xcd * ipx, i1 = min(i0 + ipx, nitems);
   int64_t j = i0 + sl;
-  if (j >= i1) return;                                  // uniform per workgroup
+  if (!LDS_TABLE && j >= i1) return;                    // uniform per workgroup
   if (tid < (kMaxShift + 1) * 2) {
     const int d = tid >> 1, hf = tid & 1;
     uint32_t w = 0;
@@ -408,9 +463,44 @@ __global__ __launch_bounds__(kCThreads) void fp8col_tokblk_kernel(
   if constexpr (LDS_TABLE)
     for (int e = tid; e <= E; e += kCThreads) offs[e] = clampT(off[e], T);
   __syncthreads();
+  // the dense layout: thread t scans experts 2t and 2t + 1 (E + 1 <= 2 kCThreads)
+  bool dense = false;
+  if constexpr (LDS_TABLE) {
+    const int e0 = 2 * tid, e1 = e0 + 1;
+    const int a0 = e0 < E ? (max(offs[e0 + 1] - offs[e0], 0) + 127) / 128 : 0;
+    const int a1 = e1 < E ? (max(offs[e1 + 1] - offs[e1], 0) + 127) / 128 : 0;
+    int v = a0 + a1;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int t = __shfl_up(v, d);
+      v += lane >= d ? t : 0;
+    }
+    if (lane == 63) wsum[wave] = v;
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wave; ++w) base += wsum[w];
+    const int excl = base + v - (a0 + a1);
+    if (e0 <= E) pst[e0] = excl;
+    if (e1 <= E) pst[e1] = excl + a0;
+    __syncthreads();
+    const int stot = pst[E];
+    // never longer than the closed form for ordered offsets; malformed ones
+    // that would make it longer keep the closed form (and its launch sizes)
+    dense = stot <= (T + 127) / 128 + E;
+    if (dense) {
+      ntiles = (stot + 3) / 4;
+      nitems = (int64_t)ntiles * ((HB + 1) / 2);
+      const int64_t ipd = (nitems + kXcds - 1) / kXcds;
+      i0 = xcd * ipd;
+      i1 = min(i0 + ipd, nitems);
+      j = i0 + sl;
+    }
+    if (j >= i1) return;                                // uniform per workgroup
+  }
 
-  ColPlan cur = plan_item<LDS_TABLE, 128>(off, offs, E, T, (int)(j % ntiles), (int)(j / ntiles),
-                                          lane, q1, g, q2);
+  ColPlan cur = dense ? plan_item_dense(offs, pst, E, (int)(j % ntiles), (int)(j / ntiles), lane, g, q2)
+                     : plan_item<LDS_TABLE, 128>(off, offs, E, T, (int)(j % ntiles), (int)(j / ntiles),
+                                                 lane, q1, g, q2);
   ColRegs rc;
   load_item(packed, sb, cur, HB, H, s8, rc);
 
@@ -421,8 +511,9 @@ __global__ __launch_bounds__(kCThreads) void fp8col_tokblk_kernel(
     ColPlan nxt = cur;
     ColRegs rn = rc;
     if (more) {
-      nxt = plan_item<LDS_TABLE, 128>(off, offs, E, T, (int)(jn % ntiles), (int)(jn / ntiles),
-                                      lane, q1, g, q2);
+      nxt = dense ? plan_item_dense(offs, pst, E, (int)(jn % ntiles), (int)(jn / ntiles), lane, g, q2)
+                  : plan_item<LDS_TABLE, 128>(off, offs, E, T, (int)(jn % ntiles), (int)(jn / ntiles),
+                                              lane, q1, g, q2);
       load_item(packed, sb, nxt, HB, H, s8, rn);
     }
     // 1. block targets (tokens outside the experts load byte 0, which never raises a max)
@@ -437,6 +528,7 @@ __global__ __launch_bounds__(kCThreads) void fp8col_tokblk_kernel(
       if (lane == 0 && (wave & 3) == 0) {
         slot_u[slot] = cur.u1;
         slot_n[slot] = cur.n1;
+        slot_b[slot] = (cur.off1 + 127) / 128 + cur.e1;
       }
     }
     lds_barrier();
@@ -471,9 +563,8 @@ __global__ __launch_bounds__(kCThreads) void fp8col_tokblk_kernel(
       const int u = slot_u[ts], n = slot_n[ts];
       const int64_t h = 256 * (int64_t)cur.bp + c;
       if (h < H && u >= 0 && u < n) {
-        const int64_t P = (int64_t)(j % ntiles) * kCTile + 128 * ts;   // the slot's first position
         const int64_t nb = (n + 127) / 128;
-        sc_out[H * ((P - u) / 128) + h * nb + u / 128] =
+        sc_out[H * (int64_t)slot_b[ts] + h * nb + u / 128] =
             __builtin_amdgcn_ldexpf(1.0f, (int)tmax[ts][c >> 5] - 127);
       }
     }

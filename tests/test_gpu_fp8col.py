@@ -187,6 +187,21 @@ def test_tokblk_random_scales_wide_shifts():
     check_tokblk(m, packed, sb, off, H)
 
 
+def test_tokblk_many_empty_experts_between_blocks():
+    """Experts with no tokens take no 128-position slot in the dense layout,
+    so long runs of them share one start: 80 empty experts between two
+    blocks of one tile, empty experts at both ends, and one-token experts
+    that each fill a slot."""
+    m = need_gpu()
+    H = 256
+    counts = np.zeros(600, np.int64)
+    counts[[5, 86, 87, 300, 598]] = [100, 60, 1, 129, 3]
+    counts[400:470] = 1                                   # 70 one-token experts, 70 slots
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    packed, sb = synth.random_mxfp4(int(off[-1]), H, seed=21)
+    check_tokblk(m, packed, sb, off, H)
+
+
 @pytest.mark.parametrize("E", [2047, 2048, 2600])
 def test_tokblk_expert_table_in_lds_and_in_global_memory(E):
     m = need_gpu()
